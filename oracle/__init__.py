@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for exact dense softmax attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's cpu_baseline leg, never by the GPU library, and sharing no code
+with it. See attention.py (the one-shot definition) and online_softmax.py
+(the blockwise route used to pin it).
+"""
+
+from .attention import backward, forward, scores, softmax_rows
+from .online_softmax import blockwise_forward, online_softmax_row
+
+__all__ = [
+    "forward",
+    "backward",
+    "scores",
+    "softmax_rows",
+    "blockwise_forward",
+    "online_softmax_row",
+]
