@@ -1,0 +1,202 @@
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--config 3]
+
+Workload: the causal bf16 forward at B=8, H=32, N=16384, d=128 (the "16K
+tokens x 32 heads x batch 8" shape of "FlashAttention" (tensorlab.fun), Beat
+01), inputs i.i.d. N(0, 1) from a fixed seed, resident in HBM before timing.
+A step is one fa_forward call over the whole batch; `value` is attention
+TFLOP/s = 4 N^2 d B H (halved for causal) / step time. The fwd+bwd pass at
+the same shape (fa_forward + fa_backward, 3.5x the forward FLOPs) is timed
+as well and reported under "fwd_bwd".
+
+Prints exactly one JSON line on stdout. The roofline block prices the
+forward kernel against the MI355X dense-bf16 matrix peak (2516.6 TFLOP/s:
+256 CUs x 4096 FLOP/clk x 2.4 GHz); per-launch durations come from HIP
+events recorded on the stream the kernel runs on. cpu_baseline times the fp64
+CPU oracle on a bounded sample of rows of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd (and fwd+bwd) at N=16K d=128 bf16; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU * 4096 FLOP/clk/CU * 2.4 GHz, dense bf16
+PEAK_HBM_GBS = 8000.0
+
+
+def attention_flops(B, H, N, d, causal):
+    f = 4.0 * N * N * d * B * H
+    return f / 2 if causal else f
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    return ap.parse_args()
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn `warmup` times, then `steps` timed times. Returns (total ms, per-launch ms list)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end), [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(cfg, q, k, v, target_s):
+    """Time the fp64 oracle on whole rows of the same workload until ~target_s of work."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_tiled_attention_38_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
+    heads = W.sample_heads(B, H, B * H, cfg["seed"] + 2)
+    rows = W.sample_rows(N, 1024, cfg["seed"] + 1)
+    flops, elapsed, done = 0.0, 0.0, 0
+    for b, h in heads:
+        qh = q[b, h].float().cpu().numpy()
+        kh = k[b, h].float().cpu().numpy()
+        vh = v[b, h].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.forward(qh, kh, vh, scale, causal, rows=rows)
+        elapsed += time.perf_counter() - t0
+        visible = (rows + 1) if causal else np.full_like(rows, N)
+        flops += 4.0 * d * float(visible.sum())
+        done += 1
+        if elapsed >= target_s:
+            break
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"fp64 one-shot oracle on {len(rows)} seeded rows (full score rows) of each of {done} heads "
+                  f"of the same workload; rate = algorithmic attention FLOPs of those rows "
+                  f"(4 d x visible keys) / {elapsed:.1f} s",
+        "seconds": elapsed,
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+    from exact_tiled_attention_38_amd import workloads as W
+
+    cfg = W.config(a.config)
+    B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q, k, v, do = W.make_inputs(cfg, dev, with_do=True)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    fwd = lambda: fa.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    total_ms, per = time_launches(fwd, a.steps, a.warmup, stream)
+    ms = total_ms / a.steps
+    flops = attention_flops(B, H, N, d, causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    per_sorted = sorted(per)
+    launch_avg = sum(per) / len(per)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"causal bf16 attention forward, B={B} H={H} N={N} d={d}" if causal
+            else f"bf16 attention forward, B={B} H={H} N={N} d={d}",
+            "B": B, "H": H, "N": N, "d": d, "causal": bool(causal), "scale": scale,
+        },
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "median_ms": round(per_sorted[len(per) // 2], 4),
+        "min_ms": round(per_sorted[0], 4),
+        "roofline": {
+            "kernel": "fwd_bf16_kernel",
+            "bound": "mfma",
+            "achieved": round(flops / (launch_avg * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (launch_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launch_avg_ms": round(launch_avg, 4),
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+    if not a.no_bwd and "fwd+bwd" in cfg["passes"]:
+        ws = torch.empty(fa.backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        try:
+            def fwd_bwd():
+                fa.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+                fa.backward(q, k, v, o, do, lse, causal=causal, scale=scale, workspace=ws)
+
+            fb_total, _ = time_launches(fwd_bwd, a.steps, a.warmup, stream)
+            fb_ms = fb_total / a.steps
+            fb_tf = 3.5 * flops / (fb_ms * 1e-3) / 1e12
+            result["fwd_bwd"] = {"ms_per_step": round(fb_ms, 4), "tflops": round(fb_tf, 2),
+                                 "frac_of_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4),
+                                 "flops": 3.5 * flops}
+        except RuntimeError as e:
+            result["fwd_bwd"] = {"error": str(e)}
+        del ws
+
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, a.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,11 @@
+"""Exact tiled attention for AMD MI355X (gfx950).
+
+Forward and backward of exact dense softmax attention, computed by hand-written
+HIP kernels in libfa.so (C ABI declared in include/fa.h). This package is the
+thin Python binding: it checks tensors, allocates outputs with PyTorch and
+passes device pointers and the current stream to the library.
+"""
+
+from .api import backward, backward_workspace_bytes, forward, forward_f32, status_string
+
+__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "status_string"]

@@ -1,0 +1,110 @@
+"""Python binding of libfa.so: tensor checks, output allocation, stream handoff.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels. There is no other code path:
+if the library is missing or a check fails, these functions raise.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "status_string"]
+
+
+def status_string(code):
+    return _lib.status_string(code)
+
+
+def _stream(t):
+    """The HIP stream PyTorch currently uses on t's device (work is enqueued there)."""
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(tensors, names, dtype, shape=None):
+    ref = tensors[0]
+    if shape is None:
+        if ref.dim() != 4:
+            raise ValueError(f"{names[0]} must be [B, H, N, d], got shape {tuple(ref.shape)}")
+        shape = tuple(ref.shape)
+    for t, n in zip(tensors, names):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{n} must be on a GPU device, got {t.device}")
+        if t.device != ref.device:
+            raise ValueError(f"{n} is on {t.device}, expected {ref.device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{n} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shape}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    return shape
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Exact attention forward on bf16 [B, H, N, d] tensors. Returns (o, lse).
+
+    o is bf16 [B, H, N, d]; lse is fp32 [B, H, N] (natural-log logsumexp of
+    the scaled, masked score row). scale defaults to 1/sqrt(d). `out` and
+    `lse` may be passed to write into preallocated tensors.
+    """
+    B, H, N, d = _check([q, k, v], ["q", "k", "v"], torch.bfloat16)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check([o], ["out"], torch.bfloat16, (B, H, N, d))
+    _check([l], ["lse"], torch.float32, (B, H, N))
+    rc = _lib.lib().fa_forward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_forward")
+    return o, l
+
+
+def forward_f32(q, k, v, causal=False, scale=None):
+    """Exact attention forward with fp32 inputs, arithmetic and output. Returns (o, lse)."""
+    B, H, N, d = _check([q, k, v], ["q", "k", "v"], torch.float32)
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.lib().fa_forward_f32(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_forward_f32")
+    return o, l
+
+
+def backward_workspace_bytes(B, H, N, d):
+    return int(_lib.lib().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
+    """Gradients (dq, dk, dv) of exact attention, recomputing P from lse.
+
+    q, k, v, o, do: bf16 [B, H, N, d]; lse: fp32 [B, H, N] from forward().
+    A workspace of backward_workspace_bytes() bytes is allocated unless given.
+    """
+    B, H, N, d = _check([q, k, v, o, do], ["q", "k", "v", "o", "do"], torch.bfloat16)
+    _check([lse], ["lse"], torch.float32, (B, H, N))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = backward_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes or workspace.device != q.device:
+        raise ValueError(f"workspace must hold {nbytes} bytes on {q.device}")
+    rc = _lib.lib().fa_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_backward")
+    return dq, dk, dv

@@ -1,0 +1,93 @@
+"""Build libfa.so for gfx950 with hipcc (in-tree, next to the Python binding).
+
+    python -m exact_tiled_attention_38_amd.csrc.build            # build
+    python exact_tiled_attention_38_amd/csrc/build.py --asm      # also keep the gfx950 assembly
+
+Every HIP source is compiled with packed-FP32 instructions disabled
+(-Xclang -target-feature -Xclang -packed-fp32-ops) and with hardware fp32
+atomics (-munsafe-fp-atomics); objects go to csrc/_build/, the library to
+exact_tiled_attention_38_amd/libfa.so.
+"""
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (looked in $HIPCC, /opt/rocm/bin, PATH)")
+
+
+def common_flags(extra=()):
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-munsafe-fp-atomics",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        f"-I{INCLUDE}",
+        f"-I{HERE}",
+        *extra,
+    ]
+
+
+def _compile(src, extra, keep_asm):
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(extra), "-c", os.path.join(HERE, src), "-o", obj]
+    if keep_asm:
+        cmd[1:1] = ["-save-temps=obj"]
+    r = subprocess.run(cmd, cwd=BUILD_DIR, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line only
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{err}")
+    return obj, err
+
+
+def build(extra=(), keep_asm=False, verbose=False):
+    """Compile every HIP source and link libfa.so. Always recompiles."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        results = list(ex.map(lambda s: _compile(s, tuple(extra), keep_asm), SOURCES))
+    objs = [o for o, _ in results]
+    if verbose:
+        for _, err in results:
+            if err.strip():
+                print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--asm", action="store_true", help="keep the device assembly (.s) in _build/")
+    ap.add_argument("-D", action="append", default=[], help="extra preprocessor definition")
+    ap.add_argument("-v", action="store_true")
+    a = ap.parse_args()
+    print(build(extra=[f"-D{x}" for x in a.D], keep_asm=a.asm, verbose=a.v))
+
+
+if __name__ == "__main__":
+    main()

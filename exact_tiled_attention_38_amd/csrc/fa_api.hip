@@ -1,0 +1,101 @@
+// C ABI of libfa.so: argument validation and dispatch to the kernel launchers.
+// Every check runs before any HIP call, so invalid arguments never reach the
+// device and never initialise the HIP runtime.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_launch_error[256] = "kernel launch failed";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Sizes shared by every entry point. Returns FA_OK or the first failing code.
+int check_sizes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long double elems = (long double)B * H * N * d;
+  if (elems >= 4.611686018427387904e18L) return FA_ERR_SHAPE;  // 2^62
+  const long long rows_blocks = ((long long)N + fa::kFwdRowsPerBlock - 1) / fa::kFwdRowsPerBlock;
+  if ((long double)B * H * (long double)rows_blocks >= 2147483648.0L) return FA_ERR_SHAPE;
+  // the f32 path uses 64-row blocks
+  if ((long double)B * H * (long double)(((long long)N + 63) / 64) >= 2147483648.0L) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_common(int B, int H, int N, int d, int causal, float scale) {
+  const int s = check_sizes(B, H, N, d);
+  if (s != FA_OK) return s;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  std::snprintf(g_launch_error, sizeof(g_launch_error), "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const int s = check_common(B, H, N, d, causal, scale);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const fa::Problem p{B, H, N, d, causal, scale};
+  return launch_status(fa::launch_fwd_bf16(q, k, v, o, lse, p, stream));
+}
+
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                   int H, int N, int d, int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const int s = check_common(B, H, N, d, causal, scale);
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const fa::Problem p{B, H, N, d, causal, scale};
+  return launch_status(fa::launch_fwd_f32(q, k, v, o, lse, p, stream));
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  if (check_sizes(B, H, N, d) != FA_OK) return 0;
+  return (size_t)B * H * N * (size_t)(d + 1) * sizeof(float);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+                int N, int d, int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  const int s = check_common(B, H, N, d, causal, scale);
+  if (s != FA_OK) return s;
+  const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const fa::Problem p{B, H, N, d, causal, scale};
+  return launch_status(fa::launch_bwd_bf16(q, k, v, o, dO, lse, dq, dk, dv, workspace, p, stream));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: B, H and N must be >= 1 and sizes within the library's limits";
+    case FA_ERR_UNSUPPORTED: return "unsupported argument: d must be 64 or 128 and causal 0 or 1";
+    case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be positive and finite";
+    case FA_ERR_LAUNCH: return g_launch_error;
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// vector types, the bf16 matrix-core instructions, cross-half wave exchange,
+// the LDS transpose read, and base-2 exp/log.
+//
+// Lane layouts used throughout (wave64; l = lane, h = l / 32):
+//   v_mfma_f32_32x32x16_bf16  D = A * B + C,  A 32x16, B 16x32, D 32x32
+//     A: lane l holds A[m = l % 32][k = 8h .. 8h + 7]
+//     B: lane l holds B[k = 8h .. 8h + 7][n = l % 32]
+//     D: lane l, register i holds D[m = 8 (i / 4) + 4h + (i % 4)][n = l % 32]
+//   ds_read_b64_tr_b16 (per group of 16 lanes, s = l % 16):
+//     if source lane s reads the 4 bf16 at row r0 + s / 4, columns
+//     c0 + 4 (s % 4) .. + 3 of a row-major matrix, result lane i of the group
+//     receives the 4 bf16 at rows r0 .. r0 + 3 of column c0 + i.
+// Both were checked on the device against a host matrix product / index dump.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine a per-lane value with the same lane of the other wave half
+// (lane l with lane l ^ 32) using v_permlane32_swap: after swapping x with
+// itself, the two results hold {x[l], x[l ^ 32]} in some order on every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read of 4 bf16 (see the layout note above).
+__device__ __forceinline__ bf16x4_t lds_read_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4_t*)(p));
+}
+
+__device__ __forceinline__ bf16x8_t concat8(bf16x4_t a, bf16x4_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of a pair.
+__device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
+  f32x2_t f = {a, b};
+  return __builtin_convertvector(f, bf16x2_t);
+}
+
+}  // namespace fa

@@ -1,0 +1,132 @@
+"""Seeded synthetic workloads: the five configurations, input generators,
+row samplers and the bookkeeping probe inputs.
+
+This module draws and lays out inputs only; it computes nothing of the
+attention method. Tests and the benchmark feed the same tensors to the HIP
+library and (read back to the host) to the CPU oracle.
+
+Values: i.i.d. N(0, 1), drawn as fp32 with a seeded torch.Generator on the
+device the tensors live on, then rounded to bf16 (fp32 kept for the fp32
+configuration). The oracle always reads back the exact values the GPU used,
+so parity does not depend on the generator being portable across devices.
+Seeds are 3800 + configuration id for tensors and +1 for row sampling.
+"""
+
+import numpy as np
+import torch
+
+# Shapes from the pages: 16K tokens x 32 heads x batch 8 is the "256 GiB of
+# scores and probabilities per layer" example of "FlashAttention"
+# (tensorlab.fun), Beat 01; a 100,000-token head with d = 128 is the 20 GB
+# score-matrix example of "FlashAttention — how 100K-token attention fits in
+# memory" (llmdaily.org, day 19).
+CONFIGS = {
+    1: dict(name="tiny_exact_f32_b1h1n256d64", B=1, H=1, N=256, d=64, dtype="f32", causal=False,
+            q_mult=1.0, seed=3801, passes=("fwd",)),
+    2: dict(name="fwd_noncausal_bf16_b8h32n2048d128_q4", B=8, H=32, N=2048, d=128, dtype="bf16",
+            causal=False, q_mult=4.0, seed=3802, passes=("fwd",)),
+    3: dict(name="fwd_causal_bf16_b8h32n16384d128", B=8, H=32, N=16384, d=128, dtype="bf16",
+            causal=True, q_mult=1.0, seed=3803, passes=("fwd", "fwd+bwd")),
+    4: dict(name="fwd_causal_bf16_b1h8n100000d128", B=1, H=8, N=100000, d=128, dtype="bf16",
+            causal=True, q_mult=1.0, seed=3804, passes=("fwd",)),
+    5: dict(name="bwd_causal_bf16_b4h16n4096d128", B=4, H=16, N=4096, d=128, dtype="bf16",
+            causal=True, q_mult=1.0, seed=3805, passes=("fwd", "bwd")),
+}
+
+
+def config(cid):
+    c = dict(CONFIGS[cid])
+    c["id"] = cid
+    c["scale"] = 1.0 / float(np.sqrt(c["d"]))
+    return c
+
+
+def _randn(shape, gen, device):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def make_inputs(cfg, device, with_do=False, shape=None, seed=None):
+    """Seeded (q, k, v[, do]) for a configuration dict (or an explicit shape).
+
+    bf16 tensors are drawn in fp32 and rounded; config['q_mult'] multiplies q
+    after drawing (x4 is exact in bf16). Returns contiguous tensors on device.
+    """
+    B, H, N, d = shape or (cfg["B"], cfg["H"], cfg["N"], cfg["d"])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg["seed"] if seed is None else seed)
+    out_dtype = torch.float32 if cfg.get("dtype") == "f32" else torch.bfloat16
+    names = ["q", "k", "v"] + (["do"] if with_do else [])
+    tensors = []
+    for name in names:
+        x = _randn((B, H, N, d), gen, device)
+        if name == "q" and cfg.get("q_mult", 1.0) != 1.0:
+            x.mul_(cfg["q_mult"])
+        tensors.append(x.to(out_dtype).contiguous())
+        del x
+    return tuple(tensors)
+
+
+def sample_rows(N, count, seed, tile=256):
+    """Sorted distinct query rows: `count` uniform draws plus row 0, row N-1 and
+    the first row of the last (possibly partial) tile of `tile` rows."""
+    rng = np.random.default_rng(seed)
+    base = rng.choice(N, size=min(count, N), replace=False)
+    extra = np.array([0, N - 1, ((N - 1) // tile) * tile])
+    return np.unique(np.concatenate([base, extra])).astype(np.int64)
+
+
+def sample_heads(B, H, count, seed):
+    """Seeded distinct (b, h) pairs."""
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(B * H, size=min(count, B * H), replace=False)
+    return [(int(f // H), int(f % H)) for f in sorted(flat)]
+
+
+# ---------------------------------------------------------------- bookkeeping probes
+#
+# Inputs whose exact outputs follow from which keys each query row sees, so a
+# test can check every row of a full-size configuration bit for bit:
+#   count: Q = 0 and V = 1 make every visible score 0, so O = 1 and
+#          exp(lse_i) = the number of visible keys.
+#   max:   scale 1, Q_i = 32 * (4096, 64, 1, 0, ...) and
+#          K_j = (floor(j / 4096) mod 64, floor(j / 64) mod 64, j mod 64, 0, ...)
+#          give s_ij = 32 j exactly in fp32 (every factor is exact in bf16 and
+#          every partial sum stays below 2^24); V_j[b] = bit b of j. The
+#          largest visible key dominates by e^32 per step, so the bits of O_i
+#          spell out the largest visible key index.
+#   min:   the same with Q negated: O_i spells out the smallest visible key.
+
+PROBE_BITS = 17  # 2^17 = 131072 > 100000
+
+
+def probe_inputs(kind, B, H, N, d, device, dtype=torch.bfloat16):
+    j = torch.arange(N, device=device, dtype=torch.int64)
+    q = torch.zeros((N, d), device=device, dtype=torch.float32)
+    k = torch.zeros((N, d), device=device, dtype=torch.float32)
+    v = torch.zeros((N, d), device=device, dtype=torch.float32)
+    if kind == "count":
+        k.normal_(generator=torch.Generator(device=device).manual_seed(7))
+        v.fill_(1.0)
+    elif kind in ("max", "min"):
+        sign = 1.0 if kind == "max" else -1.0
+        q[:, 0], q[:, 1], q[:, 2] = sign * 32 * 4096, sign * 32 * 64, sign * 32
+        k[:, 0] = ((j // 4096) % 64).float()
+        k[:, 1] = ((j // 64) % 64).float()
+        k[:, 2] = (j % 64).float()
+        for bit in range(PROBE_BITS):
+            v[:, bit] = ((j >> bit) & 1).float()
+    else:
+        raise ValueError(kind)
+    expand = lambda x: x.to(dtype).expand(B, H, N, d).contiguous()
+    return expand(q), expand(k), expand(v)
+
+
+def probe_scale(kind, d):
+    return 1.0 / float(np.sqrt(d)) if kind == "count" else 1.0
+
+
+def decode_probe_index(o):
+    """Key index spelled by the first PROBE_BITS columns of a probe output (0/1 each)."""
+    bits = torch.round(o[..., :PROBE_BITS].float()).to(torch.int64)
+    weights = (1 << torch.arange(PROBE_BITS, device=o.device, dtype=torch.int64))
+    return (bits * weights).sum(-1)

@@ -1,0 +1,134 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library (libfa.so, gfx950 / MI355X).
+ *
+ * What it computes. Exact dense softmax attention for every (batch b, head h)
+ * slice of contiguous [B, H, N, d] tensors:
+ *
+ *     S = scale * Q K^T          (masked: S[i][j] = -inf for key j > query i when causal)
+ *     P = softmax(S) row-wise,   O = P V,   lse[i] = ln sum_j exp(S[i][j])
+ *
+ * Sources (three web pages, cited by title and section):
+ *   "FlashAttention" (tensorlab.fun flagship module), Beat 01 "What problem
+ *       existed?": standard attention is score, mask, softmax, weight.
+ *   "FlashAttention — how 100K-token attention fits in memory" (llmdaily.org,
+ *       day 19): the softmax equation in "But softmax needs the whole row —
+ *       right?"; the tile pipeline in "FlashAttention idea"; the rescale in
+ *       "Online softmax intuition".
+ *   "Attention and KV Compression" (katajob.com), "Tiling and online softmax":
+ *       queries are loaded a block at a time, key/value blocks are streamed
+ *       past them, each tile's scores live only on chip, a running maximum,
+ *       running sum and partial output are rescaled when the maximum rises,
+ *       and only the output plus small per-row statistics reach HBM;
+ *       "Recomputation in the backward pass": gradients recompute the tiles
+ *       from Q, K, V and those statistics instead of storing P.
+ *
+ * Readings where the pages are silent (the same readings the CPU oracle uses):
+ *   - scale is the caller's; the pages' softmax has none. 1/sqrt(d) is usual.
+ *   - causal: key j is visible to query i iff j <= i (queries and keys have
+ *     the same count N). causal = 0 means no mask.
+ *   - the per-row statistic is one fp32 natural-log logsumexp per query row,
+ *     in scaled-score units.
+ *   - results are exact up to floating-point reassociation; they are not
+ *     bitwise equal to any other implementation.
+ *
+ * Conventions shared by every entry point below:
+ *   - Every tensor pointer is a DEVICE pointer (HIP global memory) owned by
+ *     the caller. The library never allocates, frees or synchronizes; all work
+ *     is enqueued on `stream` (0 = the null stream) and the call returns
+ *     before it runs.
+ *   - Layout: contiguous row-major [B, H, N, d] (d fastest); lse and the
+ *     backward's per-row D are [B, H, N] fp32. bf16 tensors hold raw IEEE
+ *     bfloat16 bit patterns (uint16).
+ *   - Outputs are fully overwritten and must not alias any input.
+ *   - Every pointer must be 16-byte aligned (the kernels use 128-bit loads).
+ *   - All argument checks run before any HIP call; a failing check returns
+ *     its code and enqueues nothing. A launch failure returns FA_ERR_LAUNCH;
+ *     fa_status_string() then includes the HIP error text (per thread).
+ *     Faults during execution surface at the caller's next synchronization.
+ *   - Supported: B, H, N >= 1; d in {64, 128}; causal in {0, 1};
+ *     0 < scale < inf; B*H*N*d < 2^62 and B*H*ceil(N/64) < 2^31.
+ *   - Thread safety: stateless apart from a per-thread error string.
+ *   - Determinism: forward outputs are bitwise reproducible run to run; in the
+ *     backward, dk and dv are too, dq is not (fp32 atomic accumulation).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or a size overflows the limits above  */
+  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or causal not in {0, 1}          */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
+  FA_ERR_SCALE = 5,       /* scale is not positive, or NaN or infinite           */
+  FA_ERR_LAUNCH = 6       /* the HIP kernel launch itself failed                  */
+};
+
+/*
+ * Forward, bf16 inputs, fp32 accumulation. The tiled online-softmax forward
+ * of "Attention and KV Compression", "Tiling and online softmax": for each
+ * block of query rows, K/V tiles are streamed through LDS, QK^T and PV run on
+ * bf16 matrix cores with fp32 accumulation, and the running max / running sum
+ * / output accumulator are rescaled by exp(m_old - m_new) when a tile raises
+ * the max ("FlashAttention — how 100K-token attention fits in memory",
+ * "Online softmax intuition"). Causal tiles wholly above the diagonal are
+ * skipped; ragged tails are predicated.
+ *   q, k, v : const bf16 [B, H, N, d]            (inputs)
+ *   o       : bf16 [B, H, N, d]                  (output; O rounded to nearest even)
+ *   lse     : fp32 [B, H, N]                     (output; natural-log logsumexp)
+ * Allocates nothing: no buffer of size O(N^2), or any other, is created.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Forward, fp32 inputs, fp32 arithmetic, fp32 output; same tiling and online
+ * softmax as fa_forward, without bf16 rounding anywhere (for checks that need
+ * fp32 accuracy). Same arguments, all tensors fp32.
+ */
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_backward needs: an fp32 dQ accumulator
+ * [B, H, N, d] followed by the fp32 per-row D = rowsum(dO * O) [B, H, N],
+ * i.e. B*H*N*(d+1)*4 bytes, O(N*d). Returns 0 for invalid sizes.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward with recomputation ("Attention and KV Compression", "Recomputation
+ * in the backward pass"; "FlashAttention — how 100K-token attention fits in
+ * memory", "Training backward"). P is never stored: each (query tile, key
+ * tile) pair recomputes S = scale Q K^T and P = exp(S - lse) from the saved
+ * lse, then
+ *     dV += P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *     dK += scale dS^T Q,  dQ += scale dS K.
+ *   q, k, v, o, dO : const bf16 [B, H, N, d]  (o and lse as fa_forward wrote them)
+ *   lse            : const fp32 [B, H, N]
+ *   dq, dk, dv     : bf16 [B, H, N, d]        (outputs)
+ *   workspace      : device scratch of fa_backward_workspace_bytes(B, H, N, d)
+ *                    bytes, 16-byte aligned; its contents on entry do not
+ *                    matter (the library clears what it uses on `stream`).
+ * Two calls may not share a workspace concurrently.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/* Static text for a status code; for FA_ERR_LAUNCH the text of the calling
+ * thread's last HIP launch error. Never NULL. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,165 @@
+"""CPU checks of the C ABI in include/fa.h: the library loads, exports every
+declared function, and rejects invalid arguments with the documented status
+codes before making any HIP call (so these run without a GPU).
+
+Every call below carries at least one invalid argument; _expect() refuses to
+make a call whose arguments would all pass validation (fake pointers must
+never reach a kernel).
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_38_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "exact_tiled_attention_38_amd", "csrc")
+
+CODES = _lib.status_codes()
+OK = CODES["FA_OK"]
+A = 0x10000  # a 16-byte aligned fake address (never dereferenced)
+
+
+def declared_functions():
+    text = open(_lib.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return _lib.lib()
+
+
+def test_status_enum_matches_documentation():
+    assert CODES == {
+        "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3,
+        "FA_ERR_ALIGN": 4, "FA_ERR_SCALE": 5, "FA_ERR_LAUNCH": 6,
+    }
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+    for name in names:
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    for name, code in CODES.items():
+        s = _lib.status_string(code)
+        assert isinstance(s, str) and s
+    assert _lib.status_string(12345) == "unknown status"
+
+
+def _prevalidate(kind, ptrs, B, H, N, d, causal, scale):
+    """Python restatement of the documented checks, in the documented order."""
+    if any(p in (None, 0) for p in ptrs):
+        return CODES["FA_ERR_NULL"]
+    if B < 1 or H < 1 or N < 1:
+        return CODES["FA_ERR_SHAPE"]
+    if d not in (64, 128):
+        return CODES["FA_ERR_UNSUPPORTED"]
+    if B * H * N * d >= 2**62 or B * H * -(-N // 64) >= 2**31:
+        return CODES["FA_ERR_SHAPE"]
+    if causal not in (0, 1):
+        return CODES["FA_ERR_UNSUPPORTED"]
+    if not (scale > 0) or not math.isfinite(scale):
+        return CODES["FA_ERR_SCALE"]
+    if any(p % 16 for p in ptrs):
+        return CODES["FA_ERR_ALIGN"]
+    return OK
+
+
+def _expect(L, fn, code, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125):
+    nptr = 10 if fn == "fa_backward" else 5
+    ptrs = [A] * nptr if ptrs is None else ptrs
+    pre = _prevalidate(fn, ptrs, B, H, N, d, causal, scale)
+    assert pre != OK, "refusing to call the library with arguments that would launch a kernel"
+    assert pre == code, (pre, code)
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs] + [B, H, N, d, causal, ctypes.c_float(scale), None]
+    rc = getattr(L, fn)(*args)
+    assert rc == code, (fn, rc, _lib.status_string(rc))
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+def test_null_pointers(L, fn):
+    n = 10 if fn == "fa_backward" else 5
+    for i in range(n):
+        ptrs = [A] * n
+        ptrs[i] = 0
+        _expect(L, fn, CODES["FA_ERR_NULL"], ptrs=ptrs)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("B,H,N", [(0, 1, 16), (1, 0, 16), (1, 1, 0), (-1, 1, 16), (1, 1, -5)])
+def test_bad_shape(L, fn, B, H, N):
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], B=B, H=H, N=N)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+def test_size_overflow(L, fn):
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], B=2**30, H=2**20, N=2**20, d=128)
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], B=65536, H=65536, N=2**10, d=64)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("d", [0, 1, 32, 63, 96, 127, 129, 256])
+def test_unsupported_head_dim(L, fn, d):
+    _expect(L, fn, CODES["FA_ERR_UNSUPPORTED"], d=d)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("causal", [-1, 2, 7])
+def test_bad_causal_flag(L, fn, causal):
+    _expect(L, fn, CODES["FA_ERR_UNSUPPORTED"], causal=causal)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), -float("inf")])
+def test_bad_scale(L, fn, scale):
+    _expect(L, fn, CODES["FA_ERR_SCALE"], scale=scale)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+def test_misaligned_pointers(L, fn):
+    n = 10 if fn == "fa_backward" else 5
+    for i in range(n):
+        for off in (2, 4, 8):
+            ptrs = [A] * n
+            ptrs[i] = A + off
+            _expect(L, fn, CODES["FA_ERR_ALIGN"], ptrs=ptrs)
+
+
+def test_workspace_bytes(L):
+    for B, H, N, d in [(4, 16, 4096, 128), (1, 1, 1, 64), (8, 32, 16384, 128), (1, 8, 100000, 128)]:
+        assert L.fa_backward_workspace_bytes(B, H, N, d) == B * H * N * (d + 1) * 4
+    for B, H, N, d in [(0, 1, 1, 64), (1, 1, 0, 64), (1, 1, 16, 96)]:
+        assert L.fa_backward_workspace_bytes(B, H, N, d) == 0
+
+
+def test_library_sources_never_allocate_device_memory():
+    # The forward must allocate nothing (no O(N^2) buffer, no hidden scratch);
+    # the backward uses only the caller's workspace.
+    banned = re.compile(r"\bhip(Malloc|MallocAsync|MallocManaged|ExtMallocWithFlags|HostMalloc|Free|FreeAsync)\b")
+    for name in os.listdir(CSRC):
+        if name.endswith((".hip", ".h", ".cpp")):
+            text = open(os.path.join(CSRC, name)).read()
+            assert not banned.search(text), name
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.forward(x, x, x)
