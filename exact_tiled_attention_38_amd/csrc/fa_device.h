@@ -41,6 +41,14 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// max(a, b, c) in one v_max3_f32 (the compiler otherwise builds a tree of
+// two-input maxima for a long chain).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Combine a per-lane value with the same lane of the other wave half
 // (lane l with lane l ^ 32) using v_permlane32_swap: after swapping x with
 // itself, the two results hold {x[l], x[l ^ 32]} in some order on every lane.

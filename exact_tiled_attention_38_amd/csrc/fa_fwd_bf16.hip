@@ -18,16 +18,38 @@
 //     plus one v_permlane32_swap.
 //   * The output is accumulated transposed too, O^T += V^T P^T: P^T comes
 //     straight from the score registers (rounded to bf16), and the V^T
-//     operand is read from V's natural row-major LDS tile with
-//     ds_read_b64_tr_b16. The contraction index order inside each 16-key MFMA
-//     step follows the score registers' key order, which the two transposed
-//     reads reproduce (rows 4h..4h+3 and 8+4h..8+4h+3 of each 16-key group).
-//   * K and V tiles (BN keys) are double-buffered in LDS; the next tile's
-//     global loads are issued before the current tile's math, and stored to
-//     the other buffer after it, so one barrier per tile suffices.
-//   * Causal: the key range of a query block ends at its last row; tiles
-//     wholly after a wave's last row are skipped by that wave; only tiles
-//     touching the diagonal or the ragged tail (keys >= N) are masked.
+//     operand is read from V's row-major LDS tile with ds_read_b64_tr_b16.
+//     The contraction index order inside each 16-key MFMA step follows the
+//     score registers' key order, which the two transposed reads reproduce
+//     (rows 4h..4h+3 and 8+4h..8+4h+3 of each 16-key group).
+//   * K and V tiles (BN keys) move from HBM to LDS with direct-to-LDS 16-byte
+//     loads (global_load_lds_dwordx4; each wave-wide load fills 1 KB of
+//     consecutive LDS), so no registers or LDS-store instructions stage them.
+//     Rows are unpadded; the 16-byte chunks of a row are XOR-swizzled by a
+//     function of the row so that both the 128-bit K reads (16 rows, one
+//     chunk column) and the transposed V reads (4 rows x 64 bytes) hit 64
+//     distinct banks. A lane of the wave-wide load fetches the global chunk
+//     that belongs at its LDS slot.
+//   * Ring of S K tiles and S V tiles in LDS, one barrier per tile. Every
+//     step issues the loads of tiles several steps ahead and waits (vmcnt)
+//     only for the ones the next step reads. The loads are inline assembly,
+//     so the compiler neither orders nor counts them; the waits are explicit.
+//   * A step is straight-line code with an explicit instruction schedule
+//     (sched_barrier slices): the scores of tile u+1 run on the matrix cores
+//     while the vector unit runs the softmax update of tile u (exponentials,
+//     row sum, bf16 rounding of P) and the accumulator rescale by alpha, one
+//     slice per matrix instruction; then P(u) V(u) accumulates. LDS reads
+//     are issued a few matrix instructions ahead.
+//   * Waves w and w + 4 share a SIMD. The upper half of the workgroup runs
+//     the same steps shifted by half a tile (PV of the previous tile first),
+//     so one wave of a SIMD feeds the matrix core while the other runs its
+//     exponentials.
+//   * Every wave runs every tile of the workgroup's key range: a tile wholly
+//     after a wave's rows is masked entirely (alpha = 1, P = 0, acc and l
+//     unchanged), which keeps the loop free of branches around the work.
+//   * Causal: the key range of a query block ends at its last row; only tiles
+//     touching the diagonal or the ragged tail (keys >= N) are masked. Tail
+//     rows are loaded from the clamped key N-1 (finite values) and masked.
 //   * Grid order: workgroups are dispatched round-robin over the 8 XCDs; the
 //     block index is remapped so each XCD works through whole heads (K/V of a
 //     head stay in that XCD's L2), longest causal query blocks first.
@@ -35,36 +57,99 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#ifndef FA_FWD_BN
+#define FA_FWD_BN 64
+#endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 4
+#endif
+// Tuning switches (all settings compute the same result):
+// 1: the accumulator rescale is spread over the score/softmax slices (always
+// done); 0: it is a separate block skipped when no row's maximum rose
+#ifndef FA_FWD_RESCALE_IN_SLICES
+#define FA_FWD_RESCALE_IN_SLICES 1
+#endif
+// 1: the upper half of the workgroup runs its steps half a tile shifted
+#ifndef FA_FWD_PINGPONG
+#define FA_FWD_PINGPONG 1
+#endif
+
 namespace fa {
 namespace {
 
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, int S>
 struct FwdCfg {
-  static constexpr int BM = 32 * NW;        // query rows per workgroup
-  static constexpr int NT = 64 * NW;        // threads
-  static constexpr int KSTRIDE = D + 8;     // bf16 per K row in LDS (16 B pad: conflict-free 128-bit row reads)
-  static constexpr int VSTRIDE = D + 32;    // bf16 per V row in LDS (row pitch = 16 banks mod 64: conflict-free transposed reads)
-  static constexpr int KTILE = BN * KSTRIDE;
-  static constexpr int VTILE = BN * VSTRIDE;
-  static constexpr int BUF = KTILE + VTILE; // one K+V buffer, in bf16 elements
-  static constexpr int CHUNKS = BN * D / 8; // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = CHUNKS / NT;   // chunks per thread per tensor
-  static constexpr int LDS_ELEMS = 2 * BUF;
-  static_assert(CHUNKS % NT == 0, "tile must split evenly over threads");
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static constexpr int BM = 32 * NW;              // query rows per workgroup
+  static constexpr int NT = 64 * NW;              // threads
+  static constexpr int ROWB = 2 * D;              // bytes per K/V row in LDS (unpadded)
+  static constexpr int TILEB = BN * ROWB;         // bytes per K (or V) tile
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int RPW = 1024 / ROWB;         // rows filled by one wave-wide 1 KB load
+  static constexpr int NDMA = TILEB / 1024 / NW;  // wave-wide loads per wave, per tile and tensor
+  static constexpr int STAGES = S;                // K and V tiles resident in LDS (ring)
+  static constexpr int LDS_BYTES = 2 * S * TILEB; // K slots 0..S-1, then V slots 0..S-1
+  // DMAs a wave may leave in flight at the end of a step: the tiles issued
+  // after the ones the next step reads (see the pipeline below)
+  static constexpr int INFLIGHT = (2 * S - 5) * NDMA;
+  static_assert(TILEB % (1024 * NW) == 0, "a tile must split into whole wave-wide loads");
+  static_assert(S >= 4 && (S & (S - 1)) == 0 && INFLIGHT <= 63, "stages: power of two >= 4, vmcnt range");
+  static_assert(NW % 2 == 0, "two halves of the workgroup share the SIMDs");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
 };
 
-template <int D, int NW, int BN, bool CAUSAL>
+// Chunk swizzles (XOR on the 16-byte chunk index within a row). RPL = rows
+// per 256-byte bank line. K: the 16 rows of one 128-bit read phase land on 16
+// distinct chunk slots. V: the 4 rows of one transposed read phase land in 4
+// distinct 64-byte quarters of the bank line.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  constexpr int RPL = 128 / D;
+  return (r / RPL) & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int RPL = 128 / D;
+  return 4 * ((r / RPL) & (4 / RPL - 1));
+}
+
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane i reads base + voff (its own offset) and writes LDS byte lds + 16 i.
+// Written as inline assembly so that the compiler neither tracks these
+// writes to LDS (it would otherwise wait for every outstanding load before
+// each LDS read) nor counts them; the pipeline waits for them explicitly
+// with wait_loads_and_barrier. M0 carries the wave-uniform LDS address.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, FA_LDS char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(la) : "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations are still
+// outstanding (they complete in issue order) and all of its LDS reads have
+// returned, then join the workgroup barrier. After the barrier other waves
+// may overwrite the ring slots this wave just read. No memory fence: LDS
+// visibility is all that is needed.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <int D, int NW, int BN, int S, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int N, int n_qtiles, float c2) {
-  using C = FwdCfg<D, NW, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_ELEMS];
+  using C = FwdCfg<D, NW, BN, S>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  FA_LDS char* lds = (FA_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int h = lane >> 5;  // which 16 of each 32 keys this lane holds
   const int n = lane & 31;  // this lane's query row within the wave
 
@@ -72,16 +157,59 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int G = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, jx = b >> 3, per = G >> 3, rem = G & 7;
   const int logical = xcd * per + min(xcd, rem) + jx;
-  const int bh = logical / n_qtiles;
+  // (integer division runs on the vector unit; the results are uniform, so
+  // move them back to scalar registers and keep all tile bookkeeping scalar)
+  const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
   int t = logical - bh * n_qtiles;
   if (CAUSAL) t = n_qtiles - 1 - t;
-  const int q0 = t * C::BM;
-  const int row0 = q0 + 32 * w;
+  const int q0 = __builtin_amdgcn_readfirstlane(t * C::BM);
+  const int row0 = __builtin_amdgcn_readfirstlane(q0 + 32 * w);
   const int qrow = row0 + n;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+
+  // ---- direct-to-LDS tile loads. Lane `lane` of wave-wide load i fills the
+  // 16-byte LDS slot `lane` of 1 KB block w * NDMA + i of the tile buffer:
+  // row r of the tile, physical chunk lane % CPR, so it fetches the global
+  // chunk whose swizzled position that is. Byte offsets within a tile
+  // (row r * ROWB + chunk * 16) are kept per lane; the tile base is scalar.
+  uint32_t dk_off[C::NDMA], dv_off[C::NDMA];
+#pragma unroll
+  for (int i = 0; i < C::NDMA; ++i) {
+    const int r = (w * C::NDMA + i) * C::RPW + lane / C::CPR;
+    const int phys = lane % C::CPR;
+    dk_off[i] = r * C::ROWB + 16 * (phys ^ kswz<D>(r));
+    dv_off[i] = r * C::ROWB + 16 * (phys ^ vswz<D>(r));
+  }
+  // rows past the last key (tail tile) are fetched from key N-1 instead:
+  // finite values that the mask then excludes
+  auto clamp_row = [&](uint32_t off, int lim) {
+    return (uint32_t)min((int)(off / C::ROWB), lim) * C::ROWB + (off % C::ROWB);
+  };
+  // Tile t goes to ring slot t % S. Past the last tile the loads repeat the
+  // last tile into the (unused) slot, so every step issues the same number
+  // of loads and the wait count below is a constant.
+  auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA]) {
+    const int slot = slot0 + (t & (S - 1));
+    const int k0 = min(t, n_tiles - 1) * BN;
+    const char* base = (const char*)(src + (size_t)k0 * D);
+    FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024;
+    if (k0 + BN <= N) {
+#pragma unroll
+      for (int i = 0; i < C::NDMA; ++i) dma16(base, off[i], dst + i * 1024);
+    } else {
+      const int lim = N - 1 - k0;
+#pragma unroll
+      for (int i = 0; i < C::NDMA; ++i) dma16(base, clamp_row(off[i], lim), dst + i * 1024);
+    }
+  };
+  auto load_k = [&](int t) { load_tile(Kh, t, 0, dk_off); };
+  auto load_v = [&](int t) { load_tile(Vh, t, S, dv_off); };
 
   // ---- Q^T operand: lane holds Q[qrow][16c + 8h .. +7]
   bf16x8_t qf[D / 16];
@@ -91,38 +219,22 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (qrow < N) x = *(const u32x4_t*)(Qh + (size_t)qrow * D + 16 * c + 8 * h);
     qf[c] = __builtin_bit_cast(bf16x8_t, x);
   }
-
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-
-  // ---- K/V tile staging: thread handles 16-byte chunks tid + i*NT
-  u32x4_t kr[C::CPT], vr[C::CPT];
-  auto gload = [&](int u) {
+  // take delivery of Q before the tile loads start, so the wait for Q does
+  // not also wait for the tiles queued behind it
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::NT;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      const int key = u * BN + r;
-      u32x4_t zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        zk = *(const u32x4_t*)(Kh + (size_t)key * D + cc * 8);
-        zv = *(const u32x4_t*)(Vh + (size_t)key * D + cc * 8);
-      }
-      kr[i] = zk;
-      vr[i] = zv;
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * C::BUF;
-    uint16_t* Vs = Ks + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::NT;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      *(u32x4_t*)(Ks + r * C::KSTRIDE + cc * 8) = kr[i];
-      *(u32x4_t*)(Vs + r * C::VSTRIDE + cc * 8) = vr[i];
-    }
-  };
+  for (int c = 0; c < D / 16; ++c) asm volatile("" :: "v"(qf[c]));
+
+  // LDS read offsets (bytes, within a tile buffer).
+  // K: row kb*32 + n, logical chunk 2c + h, at koff0 ^ (32 c): the swizzle
+  // only permutes the chunk index bits above the lowest one, so the offset
+  // for d-chunk c is one XOR away from that of chunk 0.
+  const int koff0 = n * C::ROWB + 16 * (h ^ kswz<D>(n));
+  // V (transposed reads): row 4h + q, q = (lane >> 2) & 3 (plus a multiple
+  // of 16, and 8 more for the upper half); columns 32j + 16x + 4(lane & 3),
+  // x = (lane >> 4) & 1, at voff0 ^ (64 j).
+  const int tr_row = 4 * h + ((lane >> 2) & 3);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int voff0 = tr_row * C::ROWB + 16 * (tr_chunk ^ vswz<D>(tr_row)) + 8 * (lane & 1);
 
   float m_run = -INFINITY;  // running max of s2 for row qrow
   float l_run = 0.f;        // running sum of 2^(s2 - m_run) over this lane's keys
@@ -132,92 +244,249 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // LDS byte addresses of this lane's K row (chunk 0) and V row (d-block 0)
+  // in ring slot `buf`: a slot base is a multiple of 1 KB, so the XOR on bits
+  // 5..7 that selects a chunk commutes with adding it.
+  auto k_addr = [&](int buf) { return (int)(uintptr_t)(lds + buf * C::TILEB) + koff0; };
+  auto v_addr = [&](int buf) { return (int)(uintptr_t)(lds + (S + buf) * C::TILEB) + voff0; };
 
-  for (int u = 0; u < n_tiles; ++u) {
-    if (u + 1 < n_tiles) gload(u + 1);
-    const int k0 = u * BN;
-    const bool active = (row0 < N) && (!CAUSAL || k0 <= row0 + 31);
-    if (active) {
-      const uint16_t* Ks = smem + (u & 1) * C::BUF;
-      const uint16_t* Vs = Ks + C::KTILE;
-
-      // S^T = K Q^T for BN keys x 32 queries
-      f32x16_t s[BN / 32];
+  // S^T = K Q^T for the BN keys of the K tile at LDS address kb0
+  auto qk = [&](int kb0, f32x16_t (&s)[BN / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const FA_LDS char* kp = (FA_LDS char*)(uintptr_t)(kb0 ^ (32 * c));
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
+        const bf16x8_t a = *(const FA_LDS bf16x8_t*)(kp + kb * 32 * C::ROWB);
+        s[kb] = mfma_32x32x16(a, qf[c], s[kb]);
+      }
+    }
+  };
+
+  // causal / tail mask of the tile starting at key k0: key j is kept iff
+  // j <= qrow (causal) and j < N, i.e. (j - k0 - 4h) <= lim below
+  auto mask = [&](int k0, f32x16_t (&s)[BN / 32]) {
+    const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * h;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8_t a = *(const bf16x8_t*)(Ks + (kb * 32 + n) * C::KSTRIDE + 16 * c + 8 * h);
-          s[kb] = mfma_32x32x16(a, qf[c], s[kb]);
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
+  };
+
+  // online softmax update of one tile: new max, P (bf16), l, acc rescale.
+  // Split in two so the row max can be issued ahead of the matrix work.
+  // (a chain of three-input maxima: one instruction per two scores)
+  auto row_max = [&](const f32x16_t (&s)[BN / 32]) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int f = 2; f < BN / 2; f += 2) mx = max3(mx, s[f >> 4][f & 15], s[f >> 4][(f + 1) & 15]);
+    return halves_max(mx);
+  };
+
+  // ---- the step's pieces, each an explicit instruction schedule: LDS reads
+  // run a few matrix instructions ahead, and every slice ends in a
+  // scheduling barrier so the compiler keeps the order (it schedules freely
+  // within a slice).
+  constexpr int KQ = BN / 32 * D / 16;   // score MFMAs per tile
+  constexpr int KP = BN / 16 * D / 32;   // PV MFMAs per tile
+  constexpr int VPS = (BN / 2) / KQ;     // softmax values per lane per score MFMA
+  constexpr int LA_K = 3, LA_V = 2;      // read lookahead (MFMAs)
+  static_assert(VPS % 2 == 0, "slicing");
+  // score MFMA i: d-chunk c = i / (BN/32), key block kb = i % (BN/32)
+  auto kread = [&](int kb0, int i) {
+    const int c = i / (BN / 32), kb = i % (BN / 32);
+    return *(const FA_LDS bf16x8_t*)((FA_LDS char*)(uintptr_t)(kb0 ^ (32 * c)) + kb * 32 * C::ROWB);
+  };
+  // PV MFMA k: d-block j = k / (BN/16), 16-key group kc = k % (BN/16)
+  auto vread = [&](int vb0, int k) {
+    const int j = k / (BN / 16), kc = k % (BN / 16);
+    const FA_LDS char* vp = (FA_LDS char*)(uintptr_t)(vb0 ^ (64 * j)) +
+                            ((kc >> 1) * 32 + 16 * (kc & 1)) * C::ROWB;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4_t*)vp);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4_t*)(vp + 8 * C::ROWB));
+    return concat8(lo, hi);
+  };
+
+  // Scores of the next tile (K at kb0) on the matrix cores, interleaved
+  // slice by slice with the softmax of the current tile on the vector unit
+  // (exponentials, row sum, bf16 rounding of P). Returns the row sum.
+  auto qk_softmax = [&](int kb0, float m_use, float alpha, const f32x16_t (&s_cur)[BN / 32],
+                        f32x16_t (&s_nxt)[BN / 32], bf16x8_t (&p)[BN / 16]) {
+    bf16x8_t kr[KQ];
+#pragma unroll
+    for (int i = 0; i < LA_K; ++i) kr[i] = kread(kb0, i);
+    float lsum = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      if (i + LA_K < KQ) kr[i + LA_K] = kread(kb0, i + LA_K);
+      const int c = i / (BN / 32), kb = i % (BN / 32);
+      if (c == 0) {
+        const f32x16_t z = {};
+        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], z);
+      } else {
+        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], s_nxt[kb]);
+      }
+#pragma unroll
+      for (int e = 0; e < VPS; e += 2) {
+        const int f = i * VPS + e;  // flat index of the value within the lane's BN/2
+        const float p0 = exp2_fast(fmaf(s_cur[f >> 4][f & 15], c2, -m_use));
+        const float p1 = exp2_fast(fmaf(s_cur[f >> 4][(f + 1) & 15], c2, -m_use));
+        lsum += p0 + p1;
+        const bf16x2_t pb = to_bf16x2(p0, p1);
+        p[f >> 3][f & 7] = pb[0];
+        p[f >> 3][(f + 1) & 7] = pb[1];
+      }
+      if constexpr (FA_FWD_RESCALE_IN_SLICES) {
+        constexpr int per = D / 2 / KQ;  // accumulator values rescaled per slice
+#pragma unroll
+        for (int e = 0; e < per; ++e) {
+          const int g = i * per + e;
+          acc[g >> 4][g & 15] *= alpha;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P and the row sum are complete here: keep the compiler from sinking
+    // their computation past the branches that follow
+#pragma unroll
+    for (int i = 0; i < BN / 16; ++i) asm volatile("" :: "v"(p[i]));
+    asm volatile("" :: "v"(lsum));
+    return lsum;
+  };
 
-      // mask: only tiles that cross the diagonal or the ragged tail
-      const bool need_mask = (CAUSAL && (k0 + BN - 1 > row0)) || (k0 + BN > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if ((CAUSAL && key > qrow) || key >= N) s[kb][i] = -INFINITY;
-          }
-      }
-
-      // online softmax update
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float lsum = 0.f;
-      bf16x8_t p[BN / 16];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = exp2_fast(fmaf(s[kb][8 * jj + e], c2, -m_use));
-            const float p1 = exp2_fast(fmaf(s[kb][8 * jj + e + 1], c2, -m_use));
-            lsum += p0 + p1;
-            const bf16x2_t pb = to_bf16x2(p0, p1);
-            p[2 * kb + jj][e] = pb[0];
-            p[2 * kb + jj][e + 1] = pb[1];
-          }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+  // acc *= alpha, skipped when no row of the wave raised its maximum
+  // (alpha = 1 on every lane: multiplying would change nothing)
+  auto rescale = [&](float alpha) {
+    if (FA_FWD_RESCALE_IN_SLICES) return;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][i] *= alpha;
-
-      // O^T += V^T P^T
-      const int tr_row = 4 * h + ((lane >> 2) & 3);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int kc = 0; kc < BN / 16; ++kc) {
-        const int r = (kc >> 1) * 32 + 16 * (kc & 1) + tr_row;
-#pragma unroll
-        for (int j = 0; j < D / 32; ++j) {
-          const uint16_t* vp = Vs + r * C::VSTRIDE + 32 * j + tr_col;
-          const bf16x8_t a = concat8(lds_read_tr4(vp), lds_read_tr4(vp + 8 * C::VSTRIDE));
-          acc[j] = mfma_32x32x16(a, p[kc], acc[j]);
-        }
-      }
+        for (int e = 0; e < 16; ++e) acc[j][e] *= alpha;
     }
-    if (u + 1 < n_tiles) sstore((u + 1) & 1);
-    __syncthreads();
+  };
+
+  // acc += P V for the V tile at vb0
+  auto pv = [&](int vb0, const bf16x8_t (&p)[BN / 16]) {
+    bf16x8_t vr[KP];
+#pragma unroll
+    for (int k = 0; k < LA_V; ++k) vr[k] = vread(vb0, k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      if (k + LA_V < KP) vr[k + LA_V] = vread(vb0, k + LA_V);
+      const int j = k / (BN / 16), kc = k % (BN / 16);
+      acc[j] = mfma_32x32x16(vr[k], p[kc], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- pipeline over key tiles. K(t) and V(t) live in ring slot t % S.
+  // Two schedules share the SIMDs: the workgroup's waves w and w + 4 run on
+  // the same SIMD, and the upper half runs its step shifted by half a tile.
+  //   lower half, step u: softmax(u) with the scores of tile u+1, rescale,
+  //                       then P(u) V(u)                  (vector, then matrix)
+  //   upper half, step u: P(u-1) V(u-1), then softmax(u) with the scores of
+  //                       tile u+1, rescale               (matrix, then vector)
+  // so while one wave of a SIMD runs its exponentials the other feeds the
+  // matrix core, and the other way round. Both compute the same thing: acc
+  // gains P(t) V(t) before the rescale by alpha(t+1) in either order.
+  // Step u reads K(u+1) and V(u) (lower) or V(u-1) (upper), and issues
+  // V(u+S-2) and K(u+S): V(u+S-2) replaces V(u-2), last read in step u-1;
+  // K(u+S) replaces K(u), last read in step u-1 (every wave passed that
+  // step's closing barrier). Loads are issued in the order
+  // K0 V0 K1 V1 ... K(S-3) V(S-3) K(S-2) K(S-1), then V(u+S-2) K(u+S) per
+  // step; at the end of step u the next step needs V(u+1) (and the older
+  // K(u+2)), after which 2S-5 tiles' loads were issued, so each wave waits
+  // until at most that many DMAs are outstanding, then the barrier publishes
+  // the tiles to all waves.
+#pragma unroll
+  for (int t = 0; t + 2 < S; ++t) {
+    load_k(t);
+    load_v(t);
   }
+  load_k(S - 2);
+  load_k(S - 1);
+  wait_loads_and_barrier<C::INFLIGHT>();
+
+  f32x16_t sA[BN / 32], sB[BN / 32];
+  bf16x8_t pA[BN / 16], pB[BN / 16];
+  qk(k_addr(0), sA);
+
+  // Every wave runs every step of the workgroup's key range, with no
+  // branch around the work: a tile wholly after a wave's rows (or past N)
+  // is masked entirely, which leaves m and l unchanged, gives alpha = 1
+  // exactly and P = 0, so acc is unchanged too. A straight path keeps the
+  // accumulator in the same registers through the loop. The step count is
+  // rounded up to even (the extra step is such a masked tile) so the
+  // two-step loop body needs no exit in its middle. Scores of tile u+1 are
+  // computed in step u even past the last tile: the ring slot then holds a
+  // repeat of the last tile, finite data whose scores go unused.
+  //
+  // Common head of a step: loads, mask, this step's LDS addresses (through
+  // an empty asm statement so the per-chunk XORs are formed here rather than
+  // kept live across the loop), row max and alpha.
+  auto step_head = [&](int u, f32x16_t (&s_cur)[BN / 32], int& kb0, int& vb0, int v_tile,
+                  float& m_use, float& alpha) {
+    load_v(u + S - 2);
+    load_k(u + S);
+    const int k0 = u * BN;
+    if ((CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
+    kb0 = k_addr((u + 1) & (S - 1));
+    vb0 = v_addr(v_tile & (S - 1));
+    asm volatile("" : "+v"(kb0), "+v"(vb0));
+    const float mx = row_max(s_cur);
+    const float m_new = fmaxf(m_run, mx * c2);
+    m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha = exp2_fast(m_run - m_use);
+    m_run = m_new;
+  };
+  auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
+                     bf16x8_t (&p)[BN / 16]) {
+    int kb0, vb0;
+    float m_use, alpha;
+    step_head(u, s_cur, kb0, vb0, u, m_use, alpha);
+    const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
+    l_run = l_run * alpha + lsum;
+    rescale(alpha);
+    pv(vb0, p);
+    wait_loads_and_barrier<C::INFLIGHT>();
+  };
+  auto step_hi = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
+                     bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first) {
+    int kb0, vb0;
+    float m_use, alpha;
+    step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha);
+    if (!first) pv(vb0, p_prev);
+    const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
+    l_run = l_run * alpha + lsum;
+    rescale(alpha);
+    wait_loads_and_barrier<C::INFLIGHT>();
+  };
+
+  const int n_steps = (n_tiles + 1) & ~1;
+  if (!FA_FWD_PINGPONG || w < NW / 2) {
+    for (int u = 0; u < n_steps; u += 2) {
+      step_lo(u, sA, sB, pA);
+      step_lo(u + 1, sB, sA, pB);
+    }
+  } else {
+    step_hi(0, sA, sB, pA, pB, true);
+    for (int u = 1; u + 1 < n_steps; u += 2) {
+      step_hi(u, sB, sA, pB, pA, false);
+      step_hi(u + 1, sA, sB, pA, pB, false);
+    }
+    step_hi(n_steps - 1, sB, sA, pB, pA, false);
+    pv(v_addr((n_steps - 1) & (S - 1)), pB);
+  }
+  // no load may still be writing this workgroup's LDS when it exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l)
   if (qrow < N) {
@@ -237,14 +506,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, int BN, int S, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse,
                   const Problem& p, hipStream_t stream) {
-  using C = FwdCfg<D, NW, BN>;
+  using C = FwdCfg<D, NW, BN, S>;
   const int n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.B * p.H * n_qtiles;
   const float c2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, S, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                      p.N, n_qtiles, c2);
   return hipGetLastError();
@@ -254,12 +523,13 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const Problem& p, hipStream_t stream) {
-  static_assert(FwdCfg<128, 8, 64>::BM == kFwdRowsPerBlock, "grid-size limit assumes 256-row blocks");
+  static_assert(FwdCfg<128, 8, FA_FWD_BN, FA_FWD_STAGES>::BM == kFwdRowsPerBlock,
+                "grid-size limit assumes 256-row blocks");
   if (p.d == 128)
-    return p.causal ? launch<128, 8, 64, true>(q, k, v, o, lse, p, stream)
-                    : launch<128, 8, 64, false>(q, k, v, o, lse, p, stream);
-  return p.causal ? launch<64, 8, 64, true>(q, k, v, o, lse, p, stream)
-                  : launch<64, 8, 64, false>(q, k, v, o, lse, p, stream);
+    return p.causal ? launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, true>(q, k, v, o, lse, p, stream)
+                    : launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, false>(q, k, v, o, lse, p, stream);
+  return p.causal ? launch<64, 8, 64, 4, true>(q, k, v, o, lse, p, stream)
+                  : launch<64, 8, 64, 4, false>(q, k, v, o, lse, p, stream);
 }
 
 }  // namespace fa

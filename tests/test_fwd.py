@@ -119,6 +119,28 @@ def test_forward_is_deterministic(run_config2):
         assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_is_deterministic_ragged(causal):
+    # a ragged length (not a multiple of any tile), every output rewritten
+    # from a NaN-filled buffer on each run
+    _say("determinism ragged", causal)
+    B, H, N, d = 2, 3, 1000, 128
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=8), DEV, shape=(B, H, N, d))
+    ref = None
+    for _ in range(8):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((B, H, N), float("nan"), device=DEV)
+        forward(q, k, v, causal=causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o.float()).any() and not torch.isnan(lse).any()
+        if ref is None:
+            ref = (o.clone(), lse.clone())
+            continue
+        diff = (o.view(torch.int16) != ref[0].view(torch.int16)).any(-1).nonzero()
+        assert diff.shape[0] == 0, f"rows differing between runs: {diff.shape[0]}, first {diff[:6].tolist()}"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32))
+
+
 # ---------------------------------------------------------------- configuration 3
 
 
