@@ -11,21 +11,20 @@
 // derivative of the score/softmax/weight definition).
 //
 // Three kernels on the caller's stream:
-//   1. preprocess: D_i = sum_k dO_ik O_ik (fp32) and zero the fp32 dQ accumulator.
-//   2. dkdv: one workgroup per block of 128 keys of one head, 4 waves x 32 keys.
-//      K and V rows of the wave stay in registers (the B operands of S = Q K^T
-//      and dP = dO V^T); the fp32 dK^T and dV^T accumulators stay in registers
-//      for the whole key block. Query tiles of 64 rows stream through LDS
-//      (Q, dO, lse, D). In this orientation each lane owns one key and 16 of
-//      every 32 queries, so P and dS feed the dV^T = dO^T P and dK^T = Q^T dS
-//      products straight from registers, with dO^T and Q^T read from the
-//      row-major LDS tiles by ds_read_b64_tr_b16. dS^T (bf16) is staged in LDS
-//      and the workgroup then forms its 64 x d slice of dS K (the keys are the
-//      contraction) and adds it to the fp32 dQ accumulator with atomics.
-//      Causal: query tiles that end before the key block starts are never
-//      visited; waves whose keys all follow the tile's last query skip it.
-//   3. dq_convert: dQ accumulator -> bf16 dq.
-// dk and dv are deterministic; dq is not (atomic accumulation order).
+//   1. preprocess: D_i = sum_k dO_ik O_ik (fp32), into the caller's workspace.
+//   2. dkdv (this file): one workgroup per block of 128 keys of one head, 4
+//      waves x 32 keys. K and V rows of the wave stay in registers (the B
+//      operands of S = Q K^T and dP = dO V^T); the fp32 dK^T and dV^T
+//      accumulators stay in registers for the whole key block. Query tiles
+//      of 64 rows (Q, dO, lse, D) arrive by direct-to-LDS loads into a
+//      two-slot ring, one tile ahead. In this orientation each lane owns one
+//      key and 16 of every 32 queries, so P and dS feed the dV^T = dO^T P and
+//      dK^T = Q^T dS products straight from registers, with dO^T and Q^T
+//      read from the row-major LDS tiles by ds_read_b64_tr_b16. Causal: query
+//      tiles that end before the key block starts are never visited.
+//   3. dq (fa_bwd_dq.hip): one workgroup per block of query rows streams the
+//      key/value tiles and sums its rows' dQ itself, with no atomics.
+// dq, dk and dv are all bitwise deterministic.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -36,23 +35,36 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdRows = 64;              // query rows per tile
 
-// LDS pitches (bf16 elements). Q/dO tiles are read both row-wise (128-bit) and
-// transposed (ds_read_b64_tr_b16); D + 40 keeps the 16-row 128-bit reads
-// conflict-free and limits the transposed reads to 2-way. K and dS^T are only
-// read transposed: a row pitch of 16 banks mod 64 spreads each read's 4 rows
-// over distinct banks.
+// Q and dO tiles (kBwdRows rows) arrive by direct-to-LDS loads into a
+// two-slot ring, unpadded, with the 16-byte chunks of each row XOR-swizzled
+// so that both the 128-bit row reads (16 rows, one chunk column) and the
+// transposed reads (4 rows x 64 bytes) are free of bank conflicts.
 template <int D> struct BwdCfg {
-  static constexpr int QP = D + 40;
-  static constexpr int KP = D + 32;
-  static constexpr int SP = kBwdRows + 32;
+  static constexpr int ROWB = 2 * D;                      // Q/dO tile row bytes
+  static constexpr int TILEB = kBwdRows * ROWB;           // one Q (or dO) tile
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int RPW = 1024 / ROWB;                 // rows per wave-wide 1 KB load
+  static constexpr int NDMA = TILEB / 1024 / kBwdWaves;   // wave-wide loads per wave and tensor
+  static_assert(TILEB % (1024 * kBwdWaves) == 0, "tile must split into whole wave-wide loads");
 };
+
+// Chunk swizzle of the Q/dO tiles. D = 128 (one row per 256-byte bank
+// line): bits 3..2 come from row bits 1..0 (the 4 rows of a transposed read
+// land in distinct 64-byte quarters), bits 1..0 from row bits 3..2 (16
+// consecutive rows get 16 distinct chunks). D = 64 (two rows per line): the
+// same with row bits 1 and 3..2, as row bit 0 already selects the half line.
+template <int D>
+__device__ __forceinline__ int qswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // ---------------------------------------------------------------- preprocess
 
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_preprocess_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                      float* __restrict__ Dvec, float* __restrict__ dQacc, long long rows) {
+                      float* __restrict__ Dvec, long long rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = gid / LPR;
@@ -64,52 +76,33 @@ bwd_preprocess_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict
     const bf16x8_t g = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(dO + off));
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum = fmaf((float)o[e], (float)g[e], sum);
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4_t*)(dQacc + off) = z;
-    *(f32x4_t*)(dQacc + off + 4) = z;
   }
 #pragma unroll
   for (int x = LPR / 2; x >= 1; x >>= 1) sum += __shfl_xor(sum, x, LPR);
   if (row < rows && sub == 0) Dvec[row] = sum;
 }
 
-// ---------------------------------------------------------------- dq convert
-
-__global__ void __launch_bounds__(256)
-bwd_dq_convert_kernel(const float* __restrict__ dQacc, uint16_t* __restrict__ dq, long long n8) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4_t a = *(const f32x4_t*)(dQacc + 8 * i);
-  const f32x4_t b = *(const f32x4_t*)(dQacc + 8 * i + 4);
-  const bf16x2_t p0 = to_bf16x2(a[0], a[1]), p1 = to_bf16x2(a[2], a[3]);
-  const bf16x2_t p2 = to_bf16x2(b[0], b[1]), p3 = to_bf16x2(b[2], b[3]);
-  u32x4_t out = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-  *(u32x4_t*)(dq + 8 * i) = out;
-}
-
-// ---------------------------------------------------------------- dK / dV (+ dQ)
+// ---------------------------------------------------------------- dK / dV
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kBwdWaves, 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                float* __restrict__ dQacc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                 int N, int n_kblocks, float c2, float scale) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBwdRows * C::QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[kBwdRows * C::QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[kBwdKeys * C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t dSt[kBwdKeys * C::SP];
-  __shared__ __attribute__((aligned(16))) float lse2s[kBwdRows];
-  __shared__ __attribute__((aligned(16))) float Ds[kBwdRows];
+  // ring slot s: Q tile at qd + (2s) TILEB, dO tile at qd + (2s+1) TILEB
+  __shared__ __attribute__((aligned(1024))) char qd[4 * C::TILEB];
+  __shared__ __attribute__((aligned(16))) float rowstat[2][2][kBwdRows];  // [slot][lse, D][row]
+  FA_LDS char* qdl = (FA_LDS char*)qd;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
-  const int bh = blockIdx.x / n_kblocks;
+  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x / n_kblocks);
   const int kbi = blockIdx.x - bh * n_kblocks;
-  const int kb0 = kbi * kBwdKeys;
+  const int kb0 = __builtin_amdgcn_readfirstlane(kbi * kBwdKeys);
   const int kw0 = kb0 + 32 * w;
   const int key = kw0 + n;
   const size_t head = (size_t)bh * N * D;
@@ -128,13 +121,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     kf[c] = __builtin_bit_cast(bf16x8_t, a);
     vf[c] = __builtin_bit_cast(bf16x8_t, b);
   }
-  // the workgroup's K block, row-major in LDS (for the dQ product)
-  for (int ch = tid; ch < kBwdKeys * D / 8; ch += 64 * kBwdWaves) {
-    const int r = ch / (D / 8), cc = ch % (D / 8);
-    u32x4_t x = {0u, 0u, 0u, 0u};
-    if (kb0 + r < N) x = *(const u32x4_t*)(K + head + (size_t)(kb0 + r) * D + cc * 8);
-    *(u32x4_t*)(Kt + r * C::KP + cc * 8) = x;
-  }
+  // take delivery of these loads before the tile loads start (they are not
+  // counted by the explicit waits below)
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" :: "v"(kf[c]), "v"(vf[c]));
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
@@ -142,34 +133,79 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dvacc[j][i] = 0.f; dkacc[j][i] = 0.f; }
 
+  // ---- tile loads: wave w fills 1 KB blocks w*NDMA .. of the Q and dO tiles
+  uint32_t qd_off[C::NDMA];
+#pragma unroll
+  for (int i = 0; i < C::NDMA; ++i) {
+    const int r = (w * C::NDMA + i) * C::RPW + lane / C::CPR;
+    qd_off[i] = r * C::ROWB + 16 * ((lane % C::CPR) ^ qswz<D>(r));
+  }
+  auto load_tile = [&](int q0, int slot) {
+    const char* qb = (const char*)(Qh + (size_t)q0 * D);
+    const char* gb = (const char*)(dOh + (size_t)q0 * D);
+    FA_LDS char* dq_ = qdl + (2 * slot) * C::TILEB + w * C::NDMA * 1024;
+    FA_LDS char* dg_ = qdl + (2 * slot + 1) * C::TILEB + w * C::NDMA * 1024;
+    if (q0 + kBwdRows <= N) {
+#pragma unroll
+      for (int i = 0; i < C::NDMA; ++i) {
+        dma16(qb, qd_off[i], dq_ + i * 1024);
+        dma16(gb, qd_off[i], dg_ + i * 1024);
+      }
+    } else {
+      // rows past N are fetched from row N-1 (finite) and masked below
+      const int lim = N - 1 - q0;
+#pragma unroll
+      for (int i = 0; i < C::NDMA; ++i) {
+        const uint32_t off = (uint32_t)min((int)(qd_off[i] / C::ROWB), lim) * C::ROWB + qd_off[i] % C::ROWB;
+        dma16(qb, off, dq_ + i * 1024);
+        dma16(gb, off, dg_ + i * 1024);
+      }
+    }
+    if (w < 2) {  // wave 0: the rows' logsumexp, wave 1: their D
+      const char* src = (const char*)((w == 0 ? LSE : Dvec) + (size_t)bh * N + q0);
+      dma4(src, 4u * (uint32_t)min(lane, N - 1 - q0), (FA_LDS char*)&rowstat[slot][w][0]);
+    }
+  };
+
+  // LDS read offsets within a tile (bytes). Row reads (A operand rows of S
+  // and dP): row n (+32 qb), logical chunk 2c + h, at row_off ^ (32 c).
+  const int row_off = n * C::ROWB + 16 * (h ^ qswz<D>(n));
+  // Transposed reads (dO^T, Q^T): rows 4h + q (+16 jj, +32 qb) and 8 more,
+  // columns 32 j + 16 x + 4 (lane & 3), at tr_off[hi] ^ (64 j).
   const int tr_row = 4 * h + ((lane >> 2) & 3);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_off0 = tr_row * C::ROWB + 16 * (tr_chunk ^ qswz<D>(tr_row)) + 8 * (lane & 1);
+  const int tr_off1 = (tr_row + 8) * C::ROWB + 16 * (tr_chunk ^ qswz<D>(tr_row + 8)) + 8 * (lane & 1);
+
   const int n_qtiles = (N + kBwdRows - 1) / kBwdRows;
   const int t_first = CAUSAL ? kb0 / kBwdRows : 0;
+  // a tile needs the causal / tail mask when some (query, key) pair of it is
+  // invisible: a key after a query, a key past N, or a query row past N
+  const bool keys_tail = kb0 + kBwdKeys > N;
+
+  load_tile(t_first * kBwdRows, 0);
+  wait_loads_and_barrier<0>();
 
   for (int t = t_first; t < n_qtiles; ++t) {
     const int q0 = t * kBwdRows;
-    __syncthreads();  // previous tile's readers of Qs/dOs/dSt are done
-    for (int ch = tid; ch < kBwdRows * D / 8; ch += 64 * kBwdWaves) {
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (q0 + r < N) {
-        a = *(const u32x4_t*)(Qh + (size_t)(q0 + r) * D + cc * 8);
-        b = *(const u32x4_t*)(dOh + (size_t)(q0 + r) * D + cc * 8);
-      }
-      *(u32x4_t*)(Qs + r * C::QP + cc * 8) = a;
-      *(u32x4_t*)(dOs + r * C::QP + cc * 8) = b;
-    }
-    if (tid < kBwdRows) {
-      const int q = q0 + tid;
-      // rows past N get lse = +inf, hence P = 0 and dS = 0
-      lse2s[tid] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
-      Ds[tid] = q < N ? Dvec[(size_t)bh * N + q] : 0.f;
-    }
-    __syncthreads();
+    const int slot = (t - t_first) & 1;
+    if (t + 1 < n_qtiles) load_tile(q0 + kBwdRows, slot ^ 1);
+    const FA_LDS char* Qs = qdl + (2 * slot) * C::TILEB;
+    const FA_LDS char* Gs = qdl + (2 * slot + 1) * C::TILEB;
+    const bool rows_tail = q0 + kBwdRows > N;
+    const bool need_mask = (CAUSAL && kb0 + kBwdKeys - 1 > q0) || keys_tail || rows_tail;
+    // visible queries of this lane's key: qlo <= q < qhi
+    const int qlo = CAUSAL ? key : 0;
+    const int qhi = key < N ? N : 0;
 
-    const bool active = !CAUSAL || (kw0 <= q0 + kBwdRows - 1);
-    if (active) {
+    // (the base offsets pass through an empty asm statement once per tile so
+    // the compiler forms the per-chunk XORs here instead of keeping them all
+    // live across the loop)
+    int ro = row_off, to0 = tr_off0, to1 = tr_off1;
+    asm volatile("" : "+v"(ro), "+v"(to0), "+v"(to1));
+    {
+      // (waves whose keys all follow the tile's queries run it too, fully
+      // masked: P = dS = 0, which keeps one straight path through the loop)
 #pragma unroll
       for (int qb = 0; qb < kBwdRows / 32; ++qb) {
         // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys;
@@ -179,8 +215,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-          const bf16x8_t qa = *(const bf16x8_t*)(Qs + (qb * 32 + n) * C::QP + 16 * c + 8 * h);
-          const bf16x8_t ga = *(const bf16x8_t*)(dOs + (qb * 32 + n) * C::QP + 16 * c + 8 * h);
+          const int off = qb * 32 * C::ROWB + (ro ^ (32 * c));
+          const bf16x8_t qa = *(const FA_LDS bf16x8_t*)(Qs + off);
+          const bf16x8_t ga = *(const FA_LDS bf16x8_t*)(Gs + off);
           s = mfma_32x32x16(qa, kf[c], s);
           dp = mfma_32x32x16(ga, vf[c], dp);
         }
@@ -188,13 +225,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qi = qb * 32 + 8 * g + 4 * h;
-          const f32x4_t l4 = *(const f32x4_t*)(lse2s + qi);
-          const f32x4_t d4 = *(const f32x4_t*)(Ds + qi);
+          const f32x4_t l4 = *(const FA_LDS f32x4_t*)&rowstat[slot][0][qi];
+          const f32x4_t d4 = *(const FA_LDS f32x4_t*)&rowstat[slot][1][qi];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g + e;
-            float p = exp2_fast(fmaf(s[i], c2, -l4[e]));
-            if ((CAUSAL && key > q0 + qi + e) || key >= N) p = 0.f;
+            float p = exp2_fast(fmaf(s[i], c2, -l4[e] * kLog2e));
+            if (need_mask) {
+              const int q = q0 + qi + e;
+              if (q < qlo || q >= qhi) p = 0.f;
+            }
             const float ds = p * (dp[i] - d4[e]);
             pb[i >> 3][i & 7] = (__bf16)p;
             dsb[i >> 3][i & 7] = (__bf16)ds;
@@ -203,59 +243,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         // dV^T += dO^T P and dK^T += Q^T dS (queries are the contraction)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int r = qb * 32 + 16 * jj + tr_row;
+          const int rb = (qb * 32 + 16 * jj) * C::ROWB;
 #pragma unroll
           for (int j = 0; j < D / 32; ++j) {
-            const uint16_t* gp = dOs + r * C::QP + 32 * j + tr_col;
-            const uint16_t* qp = Qs + r * C::QP + 32 * j + tr_col;
-            const bf16x8_t ga = concat8(lds_read_tr4(gp), lds_read_tr4(gp + 8 * C::QP));
-            const bf16x8_t qa = concat8(lds_read_tr4(qp), lds_read_tr4(qp + 8 * C::QP));
+            const int o0 = rb + (to0 ^ (64 * j)), o1 = rb + (to1 ^ (64 * j));
+            const bf16x8_t ga = concat8(lds_read_tr4(Gs + o0), lds_read_tr4(Gs + o1));
+            const bf16x8_t qa = concat8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
             dvacc[j] = mfma_32x32x16(ga, pb[jj], dvacc[j]);
             dkacc[j] = mfma_32x32x16(qa, dsb[jj], dkacc[j]);
           }
         }
-        // dS^T -> LDS: row = this key, 4 consecutive queries per store
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int i = 4 * g;
-          const bf16x4_t v4 = {dsb[i >> 3][i & 7], dsb[i >> 3][(i & 7) + 1], dsb[i >> 3][(i & 7) + 2],
-                               dsb[i >> 3][(i & 7) + 3]};
-          *(bf16x4_t*)(dSt + (32 * w + n) * C::SP + qb * 32 + 8 * g + 4 * h) = v4;
-        }
-      }
-    } else {
-      const u32x2_t z = {0u, 0u};
-#pragma unroll
-      for (int qb = 0; qb < kBwdRows / 32; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(u32x2_t*)(dSt + (32 * w + n) * C::SP + qb * 32 + 8 * g + 4 * h) = z;
-    }
-    __syncthreads();
-
-    // dQ[q0 .. q0+63][:] += scale * dS K over this workgroup's 128 keys.
-    // (query block, d block) pairs are spread over the waves.
-    constexpr int PAIRS = (kBwdRows / 32) * (D / 32);
-    for (int pr = w; pr < PAIRS; pr += kBwdWaves) {
-      const int qb = pr / (D / 32), j = pr % (D / 32);
-      f32x16_t acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < kBwdKeys / 16; ++kc) {
-        const int r = 16 * kc + 8 * h + ((lane >> 2) & 3);
-        const uint16_t* sp = dSt + r * C::SP + qb * 32 + tr_col;
-        const uint16_t* kp = Kt + r * C::KP + 32 * j + tr_col;
-        const bf16x8_t a = concat8(lds_read_tr4(sp), lds_read_tr4(sp + 4 * C::SP));
-        const bf16x8_t b = concat8(lds_read_tr4(kp), lds_read_tr4(kp + 4 * C::KP));
-        acc = mfma_32x32x16(a, b, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + qb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (q < N) atomicAdd(dQacc + head + (size_t)q * D + 32 * j + n, scale * acc[i]);
       }
     }
+    // the next tile's Q/dO/lse/D have landed; this tile's slot is free
+    wait_loads_and_barrier<0>();
   }
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds its key's d values in groups of 4
@@ -282,13 +283,12 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, void* workspace, const Problem& p,
                   hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
-  float* dQacc = (float*)workspace;
-  float* Dvec = dQacc + rows * D;
+  float* Dvec = (float*)workspace;
   {
     const long long threads = rows * (D / 8);
     const long long blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dO, Dvec, dQacc, rows);
+                       (const uint16_t*)o, (const uint16_t*)dO, Dvec, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -297,18 +297,12 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     const long long blocks = (long long)p.B * p.H * n_kblocks;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * kBwdWaves), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, lse, (const float*)Dvec, dQacc, (uint16_t*)dk,
-                       (uint16_t*)dv, p.N, n_kblocks, p.scale * kLog2e, p.scale);
+                       (const uint16_t*)dO, lse, (const float*)Dvec, (uint16_t*)dk, (uint16_t*)dv,
+                       p.N, n_kblocks, p.scale * kLog2e, p.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    const long long n8 = rows * D / 8;
-    const long long blocks = (n8 + 255) / 256;
-    hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float*)dQacc, (uint16_t*)dq, n8);
-  }
-  return hipGetLastError();
+  return launch_bwd_dq(q, k, v, dO, lse, Dvec, dq, p, stream);
 }
 
 }  // namespace

@@ -61,9 +61,47 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- direct global -> LDS loads, written as inline assembly so that the
+// compiler neither tracks these LDS writes (it would wait for every
+// outstanding load before each LDS read) nor counts them in its own waits;
+// kernels wait for them explicitly. M0 carries the wave-uniform LDS address.
+// Lane i reads base + voff (its own 32-bit offset) and writes LDS at
+// lds + 16 i (dma16) or lds + 4 i (dma4).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, FA_LDS char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(la) : "m0");
+}
+__device__ __forceinline__ void dma4(const char* base, uint32_t voff, FA_LDS char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(base), "s"(la) : "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations are still
+// outstanding (they complete in issue order) and all of its LDS reads have
+// returned, then join the workgroup barrier. No memory fence: LDS
+// visibility is all that is needed.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 // Transposing LDS read of 4 bf16 (see the layout note above).
 __device__ __forceinline__ bf16x4_t lds_read_tr4(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4_t*)(p));
+}
+__device__ __forceinline__ bf16x4_t lds_read_tr4(const FA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4_t*)(p));
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed, with no
+// wait for outstanding global memory operations.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8_t concat8(bf16x4_t a, bf16x4_t b) {

@@ -113,31 +113,6 @@ __device__ __forceinline__ int vswz(int r) {
   return 4 * ((r / RPL) & (4 / RPL - 1));
 }
 
-// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
-// lane i reads base + voff (its own offset) and writes LDS byte lds + 16 i.
-// Written as inline assembly so that the compiler neither tracks these
-// writes to LDS (it would otherwise wait for every outstanding load before
-// each LDS read) nor counts them; the pipeline waits for them explicitly
-// with wait_loads_and_barrier. M0 carries the wave-uniform LDS address.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* base, uint32_t voff, FA_LDS char* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)lds;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(la) : "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most N of this wave's vector-memory operations are still
-// outstanding (they complete in issue order) and all of its LDS reads have
-// returned, then join the workgroup barrier. After the barrier other waves
-// may overwrite the ring slots this wave just read. No memory fence: LDS
-// visibility is all that is needed.
-template <int N>
-__device__ __forceinline__ void wait_loads_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
-}
-
 template <int D, int NW, int BN, int S, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,

@@ -24,6 +24,11 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const void* dO, const float* lse, void* dq, void* dk, void* dv,
                            void* workspace, const Problem& p, hipStream_t stream);
 
+// dQ of the backward by its own kernel (no atomics): Dvec = rowsum(dO * O).
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* Dvec, void* dq, const Problem& p,
+                         hipStream_t stream);
+
 // Query rows per workgroup of the bf16 forward (sets the grid-size limit).
 constexpr int kFwdRowsPerBlock = 256;
 

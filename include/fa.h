@@ -48,8 +48,8 @@
  *   - Supported: B, H, N >= 1; d in {64, 128}; causal in {0, 1};
  *     0 < scale < inf; B*H*N*d < 2^62 and B*H*ceil(N/64) < 2^31.
  *   - Thread safety: stateless apart from a per-thread error string.
- *   - Determinism: forward outputs are bitwise reproducible run to run; in the
- *     backward, dk and dv are too, dq is not (fp32 atomic accumulation).
+ *   - Determinism: forward and backward outputs are bitwise reproducible run
+ *     to run (no atomics anywhere).
  */
 #ifndef FA_H
 #define FA_H
@@ -97,9 +97,9 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
                    int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_backward needs: an fp32 dQ accumulator
- * [B, H, N, d] followed by the fp32 per-row D = rowsum(dO * O) [B, H, N],
- * i.e. B*H*N*(d+1)*4 bytes, O(N*d). Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_backward needs: the fp32 per-row
+ * D = rowsum(dO * O) [B, H, N], i.e. B*H*N*4 bytes, O(N). Returns 0 for
+ * invalid sizes.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 
@@ -111,12 +111,16 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  * lse, then
  *     dV += P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
  *     dK += scale dS^T Q,  dQ += scale dS K.
+ * Three kernels run on `stream`: D, then dK/dV (one workgroup per key block
+ * streaming the query tiles), then dQ (one workgroup per query block
+ * streaming the key tiles; S and dP are recomputed there too). No atomics:
+ * dq, dk and dv are bitwise reproducible.
  *   q, k, v, o, dO : const bf16 [B, H, N, d]  (o and lse as fa_forward wrote them)
  *   lse            : const fp32 [B, H, N]
  *   dq, dk, dv     : bf16 [B, H, N, d]        (outputs)
  *   workspace      : device scratch of fa_backward_workspace_bytes(B, H, N, d)
  *                    bytes, 16-byte aligned; its contents on entry do not
- *                    matter (the library clears what it uses on `stream`).
+ *                    matter (the library writes what it reads).
  * Two calls may not share a workspace concurrently.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,

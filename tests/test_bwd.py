@@ -139,7 +139,7 @@ def test_backward_at_headline_size_one_head():
     assert torch.allclose(dv_sum, do_sum, atol=1.0, rtol=2e-2)
 
 
-def test_dk_dv_deterministic_and_workspace_contents_irrelevant():
+def test_gradients_deterministic_and_workspace_contents_irrelevant():
     _say("bwd determinism")
     B, H, N, d = 2, 3, 1000, 128
     q, k, v, do = W.make_inputs(dict(dtype="bf16", seed=8), DEV, with_do=True, shape=(B, H, N, d))
@@ -148,13 +148,12 @@ def test_dk_dv_deterministic_and_workspace_contents_irrelevant():
     _, _, dq1, dk1, dv1 = _run(q, k, v, do, True, 1 / math.sqrt(d), workspace=ws)
     ws.fill_(0x7F)
     _, _, dq2, dk2, dv2 = _run(q, k, v, do, True, 1 / math.sqrt(d), workspace=ws)
-    for name, a, b_ in (("dk", dk1, dk2), ("dv", dv1, dv2)):
+    for name, a, b_ in (("dq", dq1, dq2), ("dk", dk1, dk2), ("dv", dv1, dv2)):
         diff = (a.view(torch.int16) != b_.view(torch.int16)).nonzero()
         assert diff.shape[0] == 0, (
             f"{name} differs between runs at {diff.shape[0]} elements, first (b, h, row, col): "
             f"{diff[:6].tolist()}; max abs {(a.float() - b_.float()).abs().max().item():.3e}"
         )
-    assert torch.allclose(dq1.float(), dq2.float(), atol=1e-2, rtol=1e-2)
     _check(q, k, v, do, dq1, dk1, dv1, True, 1 / math.sqrt(d), [(0, 0), (1, 2)])
 
 
