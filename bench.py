@@ -45,7 +45,100 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (reference for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibration-copy --no-bwd` into the traffic record under profiles/")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic_causal_b8h32n16384d128.md")
+FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_launch.h"]
+COPY_BYTES = 1 << 30
+
+
+def fwd_source_hash():
+    """sha256 over the forward kernel's sources: a traffic figure is only
+    reported for the kernel it was measured on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_38_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per forward launch from the committed counter record, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        rec = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+        if rec.get("kernel_source_sha256") != fwd_source_hash():
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """Write the traffic record from a FETCH_SIZE run and a WRITE_SIZE run.
+
+    Both counters are in KiB per dispatch. Each is scaled by what it reads for
+    a plain device copy of COPY_BYTES (which reads and writes COPY_BYTES), so
+    the result is in bytes as that copy defines them."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    pick = lambda d, pat: [v for k, vs in d.items() if pat(k) for v in vs]
+    is_copy = lambda k: "copy" in k.lower() and "fwd_bf16" not in k
+    is_fwd = lambda k: "fwd_bf16_kernel" in k
+    cf, cw = max(pick(f, is_copy)), max(pick(w, is_copy))  # the 1 GiB copy is the largest copy
+    ff, fw = pick(f, is_fwd), pick(w, is_fwd)
+    fetch_scale = COPY_BYTES / (cf * 1024.0)
+    write_scale = COPY_BYTES / (cw * 1024.0)
+    fk, wk = sum(ff) / len(ff), sum(fw) / len(fw)
+    traffic = fk * 1024.0 * fetch_scale + wk * 1024.0 * write_scale
+    lines = [
+        "# HBM traffic of fwd_bf16_kernel, causal bf16 attention forward B=8 H=32 N=16384 d=128",
+        "# Two counter runs on one MI355X, from the repository root (cd /tmp && export TMPDIR=/tmp first):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-bwd --no-cpu-baseline --calibration-copy",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-bwd --no-cpu-baseline --calibration-copy",
+        "#   python bench.py --pmc-summary <out>/fetch/run_counter_collection.csv <out>/write/run_counter_collection.csv",
+        "# Counters are KiB per dispatch; each is scaled by the reading of a plain 1 GiB device copy",
+        "# (1 GiB read + 1 GiB written) in the same run.",
+        f"kernel_source_sha256: {fwd_source_hash()}",
+        f"copy_bytes: {COPY_BYTES}",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_scale: {fetch_scale:.4f}",
+        f"write_scale: {write_scale:.4f}",
+        f"fwd_fetch_kib_per_launch: {fk:.1f}",
+        f"fwd_write_kib_per_launch: {wk:.1f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"algorithmic_bytes_per_launch: {algorithmic_fwd_bytes(8, 32, 16384, 128):.0f}",
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def algorithmic_fwd_bytes(B, H, N, d):
+    """Q, K, V read once and O written once (bf16), lse written once (fp32)."""
+    return 4.0 * B * H * N * d * 2 + 4.0 * B * H * N
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -113,6 +206,9 @@ def cpu_baseline(cfg, q, k, v, target_s):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -131,6 +227,12 @@ def main():
     q, k, v, do = W.make_inputs(cfg, dev, with_do=True)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if a.calibration_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     fwd = lambda: fa.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
@@ -172,8 +274,12 @@ def main():
             "traffic": None,
             "launch_avg_ms": round(launch_avg, 4),
             "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": algorithmic_fwd_bytes(B, H, N, d),
         },
     }
+
+    if a.config == 3:
+        result["roofline"]["traffic"] = read_traffic()
 
     if not a.no_bwd and "fwd+bwd" in cfg["passes"]:
         ws = torch.empty(fa.backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
