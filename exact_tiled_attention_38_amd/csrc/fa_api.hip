@@ -69,7 +69,7 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (check_sizes(B, H, N, d) != FA_OK) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return (size_t)B * H * N * 2 * sizeof(float);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,

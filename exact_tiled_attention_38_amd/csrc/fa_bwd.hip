@@ -11,7 +11,8 @@
 // derivative of the score/softmax/weight definition).
 //
 // Three kernels on the caller's stream:
-//   1. preprocess: D_i = sum_k dO_ik O_ik (fp32), into the caller's workspace.
+//   1. preprocess: D_i = sum_k dO_ik O_ik and lse_i * log2(e) (fp32), into
+//      the caller's workspace.
 //   2. dkdv (this file): one workgroup per block of 128 keys of one head, 4
 //      waves x 32 keys. K and V rows of the wave stay in registers (the B
 //      operands of S = Q K^T and dP = dO V^T); the fp32 dK^T and dV^T
@@ -25,6 +26,8 @@
 //   3. dq (fa_bwd_dq.hip): one workgroup per block of query rows streams the
 //      key/value tiles and sums its rows' dQ itself, with no atomics.
 // dq, dk and dv are all bitwise deterministic.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -64,7 +67,8 @@ __device__ __forceinline__ int qswz(int r) {
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_preprocess_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                      float* __restrict__ Dvec, long long rows) {
+                      const float* __restrict__ LSE, float* __restrict__ Dvec,
+                      float* __restrict__ L2vec, long long rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long row = gid / LPR;
@@ -79,7 +83,10 @@ bwd_preprocess_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict
   }
 #pragma unroll
   for (int x = LPR / 2; x >= 1; x >>= 1) sum += __shfl_xor(sum, x, LPR);
-  if (row < rows && sub == 0) Dvec[row] = sum;
+  if (row < rows && sub == 0) {
+    Dvec[row] = sum;
+    L2vec[row] = LSE[row] * kLog2e;  // the dK/dV kernel's exponent offset, base 2
+  }
 }
 
 // ---------------------------------------------------------------- dK / dV
@@ -88,7 +95,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kBwdWaves, 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                const float* __restrict__ LSE, const float* __restrict__ Dvec,
+                const float* __restrict__ L2vec, const float* __restrict__ Dvec,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                 int N, int n_kblocks, float c2, float scale) {
   using C = BwdCfg<D>;
@@ -161,8 +168,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dma16(gb, off, dg_ + i * 1024);
       }
     }
-    if (w < 2) {  // wave 0: the rows' logsumexp, wave 1: their D
-      const char* src = (const char*)((w == 0 ? LSE : Dvec) + (size_t)bh * N + q0);
+    if (w < 2) {  // wave 0: the rows' lse * log2(e), wave 1: their D
+      const char* src = (const char*)((w == 0 ? L2vec : Dvec) + (size_t)bh * N + q0);
       dma4(src, 4u * (uint32_t)min(lane, N - 1 - q0), (FA_LDS char*)&rowstat[slot][w][0]);
     }
   };
@@ -179,85 +186,150 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   const int n_qtiles = (N + kBwdRows - 1) / kBwdRows;
   const int t_first = CAUSAL ? kb0 / kBwdRows : 0;
-  // a tile needs the causal / tail mask when some (query, key) pair of it is
-  // invisible: a key after a query, a key past N, or a query row past N
   const bool keys_tail = kb0 + kBwdKeys > N;
 
   load_tile(t_first * kBwdRows, 0);
   wait_loads_and_barrier<0>();
 
-  for (int t = t_first; t < n_qtiles; ++t) {
+  // One query tile. MASKED: the tile has invisible (query, key) pairs (a key
+  // after a query, a key past N, or a query row past N) and its scores are
+  // masked; the other tiles run without any mask code.
+  auto tile = [&](int t, auto masked) {
+    constexpr bool need_mask = decltype(masked)::value;
     const int q0 = t * kBwdRows;
     const int slot = (t - t_first) & 1;
     if (t + 1 < n_qtiles) load_tile(q0 + kBwdRows, slot ^ 1);
     const FA_LDS char* Qs = qdl + (2 * slot) * C::TILEB;
     const FA_LDS char* Gs = qdl + (2 * slot + 1) * C::TILEB;
-    const bool rows_tail = q0 + kBwdRows > N;
-    const bool need_mask = (CAUSAL && kb0 + kBwdKeys - 1 > q0) || keys_tail || rows_tail;
-    // visible queries of this lane's key: qlo <= q < qhi
-    const int qlo = CAUSAL ? key : 0;
-    const int qhi = key < N ? N : 0;
-
     // (the base offsets pass through an empty asm statement once per tile so
     // the compiler forms the per-chunk XORs here instead of keeping them all
     // live across the loop)
     int ro = row_off, to0 = tr_off0, to1 = tr_off1;
     asm volatile("" : "+v"(ro), "+v"(to0), "+v"(to1));
-    {
-      // (waves whose keys all follow the tile's queries run it too, fully
-      // masked: P = dS = 0, which keeps one straight path through the loop)
+
+    // The tile as an explicit schedule of four phases over its two 32-row
+    // query blocks (waves whose keys all follow the tile's queries run it
+    // too, fully masked: P = dS = 0, which keeps one straight path):
+    //   A0: S(0), dP(0)                  matrix
+    //   A1: S(1), dP(1)  with P/dS(0)    matrix + vector
+    //   B0: dV, dK(0)    with P/dS(1)    matrix + vector
+    //   B1: dV, dK(1)                    matrix
+    // Each matrix instruction closes a scheduling slice; its LDS reads are
+    // issued two slices ahead. S and dP: lane holds key `key`, queries
+    // qb*32 + 8(i/4) + 4h + i%4.
+    constexpr int NC = D / 16;       // S/dP slices per query block
+    constexpr int NB = 2 * (D / 32); // dV/dK slices per query block (jj, j)
+    auto rread = [&](const FA_LDS char* base, int qb, int c) {
+      return *(const FA_LDS bf16x8_t*)(base + qb * 32 * C::ROWB + (ro ^ (32 * c)));
+    };
+    auto tread = [&](const FA_LDS char* base, int qb, int m) {
+      const int jj = m / (D / 32), j = m % (D / 32);
+      const int rb = (qb * 32 + 16 * jj) * C::ROWB;
+      return concat8(lds_read_tr4(base + rb + (to0 ^ (64 * j))), lds_read_tr4(base + rb + (to1 ^ (64 * j))));
+    };
+    f32x16_t s[2], dp[2];
+    bf16x8_t pb[2][2], dsb[2][2];
+    // P and dS (bf16) for elements 2pr, 2pr+1 of block qb; the rows'
+    // lse * log2(e) and D come from the tile's row statistics in LDS
+    auto grad_pair = [&](int qb, int pr) {
+      const int i = 2 * pr, g = i >> 2, e = i & 3;
+      const int qi = qb * 32 + 8 * g + 4 * h + e;
+      const f32x2_t l2 = *(const FA_LDS f32x2_t*)&rowstat[slot][0][qi];
+      const f32x2_t d2 = *(const FA_LDS f32x2_t*)&rowstat[slot][1][qi];
+      const float p0 = exp2_fast(fmaf(s[qb][i], c2, -l2[0]));
+      const float p1 = exp2_fast(fmaf(s[qb][i + 1], c2, -l2[1]));
+      const bf16x2_t pp = to_bf16x2(p0, p1);
+      const bf16x2_t dd = to_bf16x2(p0 * (dp[qb][i] - d2[0]), p1 * (dp[qb][i + 1] - d2[1]));
+      pb[qb][i >> 3][i & 7] = pp[0];
+      pb[qb][i >> 3][(i & 7) + 1] = pp[1];
+      dsb[qb][i >> 3][i & 7] = dd[0];
+      dsb[qb][i >> 3][(i & 7) + 1] = dd[1];
+    };
+    // causal / tail mask of block qb: scores of invisible pairs -> -inf
+    auto mask = [&](int qb) {
+      // visible queries of this lane's key: qlo <= q < qhi
+      const int qlo = (CAUSAL ? key : 0) - q0 - qb * 32 - 4 * h;
+      const int qhi = (key < N ? N : 0) - q0 - qb * 32 - 4 * h;
 #pragma unroll
-      for (int qb = 0; qb < kBwdRows / 32; ++qb) {
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys;
-        // lane holds key `key`, queries qb*32 + 8(i/4) + 4h + i%4
-        f32x16_t s, dp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const int off = qb * 32 * C::ROWB + (ro ^ (32 * c));
-          const bf16x8_t qa = *(const FA_LDS bf16x8_t*)(Qs + off);
-          const bf16x8_t ga = *(const FA_LDS bf16x8_t*)(Gs + off);
-          s = mfma_32x32x16(qa, kf[c], s);
-          dp = mfma_32x32x16(ga, vf[c], dp);
-        }
-        bf16x8_t pb[2], dsb[2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qi = qb * 32 + 8 * g + 4 * h;
-          const f32x4_t l4 = *(const FA_LDS f32x4_t*)&rowstat[slot][0][qi];
-          const f32x4_t d4 = *(const FA_LDS f32x4_t*)&rowstat[slot][1][qi];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g + e;
-            float p = exp2_fast(fmaf(s[i], c2, -l4[e] * kLog2e));
-            if (need_mask) {
-              const int q = q0 + qi + e;
-              if (q < qlo || q >= qhi) p = 0.f;
-            }
-            const float ds = p * (dp[i] - d4[e]);
-            pb[i >> 3][i & 7] = (__bf16)p;
-            dsb[i >> 3][i & 7] = (__bf16)ds;
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (queries are the contraction)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int rb = (qb * 32 + 16 * jj) * C::ROWB;
-#pragma unroll
-          for (int j = 0; j < D / 32; ++j) {
-            const int o0 = rb + (to0 ^ (64 * j)), o1 = rb + (to1 ^ (64 * j));
-            const bf16x8_t ga = concat8(lds_read_tr4(Gs + o0), lds_read_tr4(Gs + o1));
-            const bf16x8_t qa = concat8(lds_read_tr4(Qs + o0), lds_read_tr4(Qs + o1));
-            dvacc[j] = mfma_32x32x16(ga, pb[jj], dvacc[j]);
-            dkacc[j] = mfma_32x32x16(qa, dsb[jj], dkacc[j]);
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int qo = 8 * (i >> 2) + (i & 3);
+        if (qo < qlo || qo >= qhi) s[qb][i] = -INFINITY;
       }
+    };
+
+    bf16x8_t ra[NC], rg[NC];
+    ra[0] = rread(Qs, 0, 0); rg[0] = rread(Gs, 0, 0);
+    ra[1] = rread(Qs, 0, 1); rg[1] = rread(Gs, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // A0
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int cn = c + 2;  // read two slices ahead (into block 1 at the end)
+      if (cn < NC) { ra[cn] = rread(Qs, 0, cn); rg[cn] = rread(Gs, 0, cn); }
+      else { ra[cn - NC] = rread(Qs, 1, cn - NC); rg[cn - NC] = rread(Gs, 1, cn - NC); }
+      const f32x16_t z = {};
+      s[0] = mfma_32x32x16(ra[c], kf[c], c == 0 ? z : s[0]);
+      dp[0] = mfma_32x32x16(rg[c], vf[c], c == 0 ? z : dp[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (need_mask) mask(0);
+    // A1 with the softmax gradient of block 0
+    bf16x8_t ta[NB], tg[NB];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int cn = c + 2;
+      if (cn < NC) { ra[cn] = rread(Qs, 1, cn); rg[cn] = rread(Gs, 1, cn); }
+      else { ta[cn - NC] = tread(Qs, 0, cn - NC); tg[cn - NC] = tread(Gs, 0, cn - NC); }
+      const f32x16_t z = {};
+      s[1] = mfma_32x32x16(ra[c], kf[c], c == 0 ? z : s[1]);
+      dp[1] = mfma_32x32x16(rg[c], vf[c], c == 0 ? z : dp[1]);
+#pragma unroll
+      for (int pr = c * (8 / NC); pr < (c + 1) * (8 / NC); ++pr) grad_pair(0, pr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (P and dS of block 0 are complete here: keep the compiler from sinking
+    // them past the branch below, away from these matrix instructions)
+    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(dsb[0][0]), "v"(dsb[0][1]));
+    if constexpr (need_mask) mask(1);
+    // B0 (dV^T += dO^T P, dK^T += Q^T dS over block 0) with block 1's gradient
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int mn = m + 2;
+      if (mn < NB) { ta[mn] = tread(Qs, 0, mn); tg[mn] = tread(Gs, 0, mn); }
+      else { ta[mn - NB] = tread(Qs, 1, mn - NB); tg[mn - NB] = tread(Gs, 1, mn - NB); }
+      const int jj = m / (D / 32), j = m % (D / 32);
+      dvacc[j] = mfma_32x32x16(tg[m], pb[0][jj], dvacc[j]);
+      dkacc[j] = mfma_32x32x16(ta[m], dsb[0][jj], dkacc[j]);
+#pragma unroll
+      for (int pr = m * (8 / NB); pr < (m + 1) * (8 / NB); ++pr) grad_pair(1, pr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("" :: "v"(pb[1][0]), "v"(pb[1][1]), "v"(dsb[1][0]), "v"(dsb[1][1]));
+    // B1
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int mn = m + 2;
+      if (mn < NB) { ta[mn] = tread(Qs, 1, mn); tg[mn] = tread(Gs, 1, mn); }
+      const int jj = m / (D / 32), j = m % (D / 32);
+      dvacc[j] = mfma_32x32x16(tg[m], pb[1][jj], dvacc[j]);
+      dkacc[j] = mfma_32x32x16(ta[m], dsb[1][jj], dkacc[j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the next tile's Q/dO/lse/D have landed; this tile's slot is free
     wait_loads_and_barrier<0>();
-  }
+  };
+
+  // Tiles in three runs so the common one has no mask code at all: the
+  // diagonal tiles (causal: those starting before the key block's last key),
+  // the interior tiles, then a ragged last tile. A key block reaching past N
+  // masks every tile.
+  const int t_inner = keys_tail ? n_qtiles
+                                : min(n_qtiles, CAUSAL ? (kb0 + kBwdKeys - 1) / kBwdRows + 1 : 0);
+  const int t_tail = keys_tail ? n_qtiles : (N / kBwdRows);  // first tile with rows past N
+  int t = t_first;
+  for (; t < t_inner; ++t) tile(t, std::true_type{});
+  for (; t < t_tail; ++t) tile(t, std::false_type{});
+  for (; t < n_qtiles; ++t) tile(t, std::true_type{});
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds its key's d values in groups of 4
   if (key < N) {
@@ -283,12 +355,13 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, void* workspace, const Problem& p,
                   hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
-  float* Dvec = (float*)workspace;
+  float* Dvec = (float*)workspace;  // [B, H, N] D, then [B, H, N] lse * log2(e)
+  float* L2vec = Dvec + rows;
   {
     const long long threads = rows * (D / 8);
     const long long blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dO, Dvec, rows);
+                       (const uint16_t*)o, (const uint16_t*)dO, lse, Dvec, L2vec, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -297,7 +370,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     const long long blocks = (long long)p.B * p.H * n_kblocks;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * kBwdWaves), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, lse, (const float*)Dvec, (uint16_t*)dk, (uint16_t*)dv,
+                       (const uint16_t*)dO, (const float*)L2vec, (const float*)Dvec, (uint16_t*)dk, (uint16_t*)dv,
                        p.N, n_kblocks, p.scale * kLog2e, p.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -270,7 +270,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int KQ = BN / 32 * D / 16;   // score MFMAs per tile
   constexpr int KP = BN / 16 * D / 32;   // PV MFMAs per tile
   constexpr int VPS = (BN / 2) / KQ;     // softmax values per lane per score MFMA
-  constexpr int LA_K = 3, LA_V = 2;      // read lookahead (MFMAs)
+#ifndef FA_FWD_LA_K
+#define FA_FWD_LA_K 3
+#endif
+#ifndef FA_FWD_LA_V
+#define FA_FWD_LA_V 2
+#endif
+  constexpr int LA_K = FA_FWD_LA_K, LA_V = FA_FWD_LA_V;  // read lookahead (MFMAs)
   static_assert(VPS % 2 == 0, "slicing");
   // score MFMA i: d-chunk c = i / (BN/32), key block kb = i % (BN/32)
   auto kread = [&](int kb0, int i) {

@@ -98,8 +98,8 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
 
 /*
  * Bytes of device workspace fa_backward needs: the fp32 per-row
- * D = rowsum(dO * O) [B, H, N], i.e. B*H*N*4 bytes, O(N). Returns 0 for
- * invalid sizes.
+ * D = rowsum(dO * O) [B, H, N] followed by the fp32 per-row lse * log2(e)
+ * [B, H, N], i.e. B*H*N*8 bytes, O(N). Returns 0 for invalid sizes.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 

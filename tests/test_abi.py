@@ -140,7 +140,7 @@ def test_misaligned_pointers(L, fn):
 
 def test_workspace_bytes(L):
     for B, H, N, d in [(4, 16, 4096, 128), (1, 1, 1, 64), (8, 32, 16384, 128), (1, 8, 100000, 128)]:
-        assert L.fa_backward_workspace_bytes(B, H, N, d) == B * H * N * 4
+        assert L.fa_backward_workspace_bytes(B, H, N, d) == B * H * N * 8
     for B, H, N, d in [(0, 1, 1, 64), (1, 1, 0, 64), (1, 1, 16, 96)]:
         assert L.fa_backward_workspace_bytes(B, H, N, d) == 0
 
