@@ -7,6 +7,7 @@ with it. See attention.py (the one-shot definition) and online_softmax.py
 """
 
 from .attention import backward, forward, scores, softmax_rows
+from .heads import backward_heads, forward_heads, kv_head
 from .online_softmax import blockwise_forward, online_softmax_row
 
 __all__ = [
@@ -16,4 +17,7 @@ __all__ = [
     "softmax_rows",
     "blockwise_forward",
     "online_softmax_row",
+    "kv_head",
+    "forward_heads",
+    "backward_heads",
 ]
