@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
+    ap.add_argument("--workload", choices=["gqa", "mqa"],
+                    help="instead of --config: the same causal 16K shape with 8 (gqa) or 1 (mqa) "
+                         "key/value heads shared by the 32 query heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -136,9 +139,10 @@ def pmc_summary(fetch_csv, write_csv):
     print("\n".join(lines))
 
 
-def algorithmic_fwd_bytes(B, H, N, d):
+def algorithmic_fwd_bytes(B, H, N, d, Hkv=None):
     """Q, K, V read once and O written once (bf16), lse written once (fp32)."""
-    return 4.0 * B * H * N * d * 2 + 4.0 * B * H * N
+    Hkv = H if Hkv is None else Hkv
+    return (2.0 * H + 2.0 * Hkv) * B * N * d * 2 + 4.0 * B * H * N
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -177,13 +181,14 @@ def cpu_baseline(cfg, q, k, v, target_s):
     except Exception:  # pragma: no cover
         cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
     B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
+    group = H // cfg.get("Hkv", H)
     heads = W.sample_heads(B, H, B * H, cfg["seed"] + 2)
     rows = W.sample_rows(N, 1024, cfg["seed"] + 1)
     flops, elapsed, done = 0.0, 0.0, 0
     for b, h in heads:
         qh = q[b, h].float().cpu().numpy()
-        kh = k[b, h].float().cpu().numpy()
-        vh = v[b, h].float().cpu().numpy()
+        kh = k[b, h // group].float().cpu().numpy()
+        vh = v[b, h // group].float().cpu().numpy()
         t0 = time.perf_counter()
         oracle.forward(qh, kh, vh, scale, causal, rows=rows)
         elapsed += time.perf_counter() - t0
@@ -219,8 +224,9 @@ def main():
     import exact_tiled_attention_38_amd as fa
     from exact_tiled_attention_38_amd import workloads as W
 
-    cfg = W.config(a.config)
+    cfg = W.gqa_config(a.workload) if a.workload else W.config(a.config)
     B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
+    Hkv = cfg.get("Hkv", H)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -257,8 +263,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"causal bf16 attention forward, B={B} H={H} N={N} d={d}" if causal
-            else f"bf16 attention forward, B={B} H={H} N={N} d={d}",
+            "workload": ("causal " if causal else "") + f"bf16 attention forward, B={B} H={H} "
+                        + (f"Hkv={Hkv} " if Hkv != H else "") + f"N={N} d={d}",
             "B": B, "H": H, "N": N, "d": d, "causal": bool(causal), "scale": scale,
         },
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -274,11 +280,13 @@ def main():
             "traffic": None,
             "launch_avg_ms": round(launch_avg, 4),
             "algorithmic_flops_per_launch": flops,
-            "algorithmic_bytes_per_launch": algorithmic_fwd_bytes(B, H, N, d),
+            "algorithmic_bytes_per_launch": algorithmic_fwd_bytes(B, H, N, d, Hkv),
         },
     }
+    if Hkv != H:
+        result["config"]["Hkv"] = Hkv
 
-    if a.config == 3:
+    if a.config == 3 and not a.workload:
         result["roofline"]["traffic"] = read_traffic()
 
     if not a.no_bwd and "fwd+bwd" in cfg["passes"]:

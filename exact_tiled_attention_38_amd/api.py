@@ -50,23 +50,49 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """Exact attention forward on bf16 [B, H, N, d] tensors. Returns (o, lse).
+def _kv_heads(q, k, v):
+    """Shape of q and the key/value head count: k and v are [B, Hkv, N, d], Hkv | H."""
+    B, H, N, d = _check([q], ["q"], torch.bfloat16)
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, Hkv, N, d], got shape {tuple(k.shape)}")
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"k/v have {Hkv} heads, which must divide q's {H} heads")
+    _check([k, v], ["k", "v"], torch.bfloat16, (B, Hkv, N, d))
+    if k.device != q.device:
+        raise ValueError(f"k is on {k.device}, expected {q.device}")
+    return B, H, Hkv, N, d
 
-    o is bf16 [B, H, N, d]; lse is fp32 [B, H, N] (natural-log logsumexp of
-    the scaled, masked score row). scale defaults to 1/sqrt(d). `out` and
-    `lse` may be passed to write into preallocated tensors.
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Exact attention forward on bf16 tensors. Returns (o, lse).
+
+    q is [B, H, N, d]; k and v are [B, Hkv, N, d] with Hkv dividing H (Hkv = H
+    is ordinary multi-head attention; fewer key/value heads are shared by
+    consecutive query heads). o is bf16 [B, H, N, d]; lse is fp32 [B, H, N]
+    (natural-log logsumexp of the scaled, masked score row). scale defaults
+    to 1/sqrt(d). `out` and `lse` may be passed to write into preallocated
+    tensors.
     """
-    B, H, N, d = _check([q, k, v], ["q", "k", "v"], torch.bfloat16)
+    B, H, Hkv, N, d = _kv_heads(q, k, v)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check([o], ["out"], torch.bfloat16, (B, H, N, d))
     _check([l], ["lse"], torch.float32, (B, H, N))
-    rc = _lib.lib().fa_forward(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
-        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
-    )
-    _lib.check(rc, "fa_forward")
+    if o.device != q.device or l.device != q.device:
+        raise ValueError(f"out and lse must be on {q.device}")
+    if Hkv == H:
+        rc = _lib.lib().fa_forward(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+            B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+        )
+        _lib.check(rc, "fa_forward")
+    else:
+        rc = _lib.lib().fa_forward_gqa(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+            B, H, Hkv, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+        )
+        _lib.check(rc, "fa_forward_gqa")
     return o, l
 
 
@@ -90,10 +116,13 @@ def backward_workspace_bytes(B, H, N, d):
 def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
     """Gradients (dq, dk, dv) of exact attention, recomputing P from lse.
 
-    q, k, v, o, do: bf16 [B, H, N, d]; lse: fp32 [B, H, N] from forward().
-    A workspace of backward_workspace_bytes() bytes is allocated unless given.
+    q, o, do: bf16 [B, H, N, d]; k, v: bf16 [B, Hkv, N, d] (Hkv | H, as in
+    forward()); lse: fp32 [B, H, N] from forward(). dk and dv have k's shape:
+    a shared key/value head receives the sum over its query heads. A
+    workspace of backward_workspace_bytes() bytes is allocated unless given.
     """
-    B, H, N, d = _check([q, k, v, o, do], ["q", "k", "v", "o", "do"], torch.bfloat16)
+    B, H, Hkv, N, d = _kv_heads(q, k, v)
+    _check([q, o, do], ["q", "o", "do"], torch.bfloat16)
     _check([lse], ["lse"], torch.float32, (B, H, N))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = backward_workspace_bytes(B, H, N, d)
@@ -101,10 +130,10 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < nbytes or workspace.device != q.device:
         raise ValueError(f"workspace must hold {nbytes} bytes on {q.device}")
-    rc = _lib.lib().fa_backward(
+    rc = _lib.lib().fa_backward_gqa(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+        B, H, Hkv, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
     )
-    _lib.check(rc, "fa_backward")
+    _lib.check(rc, "fa_backward_gqa")
     return dq, dk, dv

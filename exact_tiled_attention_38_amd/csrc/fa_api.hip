@@ -35,6 +35,12 @@ int check_common(int B, int H, int N, int d, int causal, float scale) {
   return FA_OK;
 }
 
+// Key/value heads: 1 <= Hkv <= H and Hkv divides H.
+int check_kv_heads(int H, int Hkv) {
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int launch_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   std::snprintf(g_launch_error, sizeof(g_launch_error), "kernel launch failed: %s", hipGetErrorString(e));
@@ -45,15 +51,21 @@ int launch_status(hipError_t e) {
 
 extern "C" {
 
-int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int N, int d, int causal, float scale, hipStream_t stream) {
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  const int s = check_common(B, H, N, d, causal, scale);
+  int s = check_common(B, H, N, d, causal, scale);
+  if (s == FA_OK) s = check_kv_heads(H, Hkv);
   if (s != FA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
-  const fa::Problem p{B, H, N, d, causal, scale};
+  const fa::Problem p{B, H, N, d, causal, scale, Hkv};
   return launch_status(fa::launch_fwd_bf16(q, k, v, o, lse, p, stream));
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, int causal, float scale, hipStream_t stream) {
+  return fa_forward_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
 }
 
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
@@ -63,7 +75,7 @@ int fa_forward_f32(const float* q, const float* k, const float* v, float* o, flo
   if (s != FA_OK) return s;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
-  const fa::Problem p{B, H, N, d, causal, scale};
+  const fa::Problem p{B, H, N, d, causal, scale, H};
   return launch_status(fa::launch_fwd_f32(q, k, v, o, lse, p, stream));
 }
 
@@ -72,24 +84,34 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * N * 2 * sizeof(float);
 }
 
-int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
-                int N, int d, int causal, float scale, hipStream_t stream) {
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+                    int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
-  const int s = check_common(B, H, N, d, causal, scale);
+  int s = check_common(B, H, N, d, causal, scale);
+  if (s == FA_OK) s = check_kv_heads(H, Hkv);
   if (s != FA_OK) return s;
   const void* ptrs[] = {q, k, v, o, dO, lse, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
-  const fa::Problem p{B, H, N, d, causal, scale};
+  const fa::Problem p{B, H, N, d, causal, scale, Hkv};
   return launch_status(fa::launch_bwd_bf16(q, k, v, o, dO, lse, dq, dk, dv, workspace, p, stream));
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+                int N, int d, int causal, float scale, hipStream_t stream) {
+  return fa_backward_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, H, H, N, d, causal, scale,
+                         stream);
 }
 
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape: B, H and N must be >= 1 and sizes within the library's limits";
+    case FA_ERR_SHAPE:
+      return "invalid shape: B, H and N must be >= 1, the key/value heads must divide H, and sizes "
+             "within the library's limits";
     case FA_ERR_UNSUPPORTED: return "unsupported argument: d must be 64 or 128 and causal 0 or 1";
     case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be positive and finite";

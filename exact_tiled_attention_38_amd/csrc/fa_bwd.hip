@@ -13,8 +13,10 @@
 // Three kernels on the caller's stream:
 //   1. preprocess: D_i = sum_k dO_ik O_ik and lse_i * log2(e) (fp32), into
 //      the caller's workspace.
-//   2. dkdv (this file): one workgroup per block of 128 keys of one head, 4
-//      waves x 32 keys. K and V rows of the wave stay in registers (the B
+//   2. dkdv (this file): one workgroup per block of 128 keys of one key/value
+//      head, 4 waves x 32 keys; with shared key/value heads it streams the
+//      query tiles of every query head of its group in turn and sums their
+//      contributions in the same registers. K and V rows of the wave stay in registers (the B
 //      operands of S = Q K^T and dP = dO V^T); the fp32 dK^T and dV^T
 //      accumulators stay in registers for the whole key block. Query tiles
 //      of 64 rows (Q, dO, lse, D) arrive by direct-to-LDS loads into a
@@ -97,7 +99,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ L2vec, const float* __restrict__ Dvec,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                int N, int n_kblocks, float c2, float scale) {
+                int N, int n_kblocks, int n_kvheads, int block_major, int group, float c2, float scale) {
   using C = BwdCfg<D>;
   // ring slot s: Q tile at qd + (2s) TILEB, dO tile at qd + (2s+1) TILEB
   __shared__ __attribute__((aligned(1024))) char qd[4 * C::TILEB];
@@ -107,14 +109,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
-  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x / n_kblocks);
-  const int kbi = blockIdx.x - bh * n_kblocks;
+  // workgroup -> (key/value head, key block); the key/value head is shared
+  // by query heads kvbh * group .. + group - 1, whose gradients it sums.
+  // Head-major by default: the key blocks of a head run side by side and
+  // share its query tiles in L2. A small grid (few key/value heads, long
+  // groups) goes key-block-major instead, so that under a causal mask the
+  // longest blocks start first and the last wave of workgroups is short.
+  int kvbh, kbi;
+  if (block_major) {
+    kbi = blockIdx.x / n_kvheads;
+    kvbh = blockIdx.x - kbi * n_kvheads;
+  } else {
+    kvbh = blockIdx.x / n_kblocks;
+    kbi = blockIdx.x - kvbh * n_kblocks;
+  }
+  kvbh = __builtin_amdgcn_readfirstlane(kvbh);
   const int kb0 = __builtin_amdgcn_readfirstlane(kbi * kBwdKeys);
   const int kw0 = kb0 + 32 * w;
   const int key = kw0 + n;
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* dOh = dO + head;
+  const size_t head = (size_t)kvbh * N * D;
+  // the query head being streamed (set per head of the group below)
+  int bh = 0;
+  const uint16_t* Qh = Q;
+  const uint16_t* dOh = dO;
 
   // this lane's key and value row as MFMA B operands: K[key][16c + 8h .. +7]
   bf16x8_t kf[D / 16], vf[D / 16];
@@ -188,8 +205,6 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int t_first = CAUSAL ? kb0 / kBwdRows : 0;
   const bool keys_tail = kb0 + kBwdKeys > N;
 
-  load_tile(t_first * kBwdRows, 0);
-  wait_loads_and_barrier<0>();
 
   // One query tile. MASKED: the tile has invisible (query, key) pairs (a key
   // after a query, a key past N, or a query row past N) and its scores are
@@ -326,10 +341,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int t_inner = keys_tail ? n_qtiles
                                 : min(n_qtiles, CAUSAL ? (kb0 + kBwdKeys - 1) / kBwdRows + 1 : 0);
   const int t_tail = keys_tail ? n_qtiles : (N / kBwdRows);  // first tile with rows past N
-  int t = t_first;
-  for (; t < t_inner; ++t) tile(t, std::true_type{});
-  for (; t < t_tail; ++t) tile(t, std::false_type{});
-  for (; t < n_qtiles; ++t) tile(t, std::true_type{});
+  for (int g = 0; g < group; ++g) {
+    bh = __builtin_amdgcn_readfirstlane(kvbh * group + g);
+    Qh = Q + (size_t)bh * N * D;
+    dOh = dO + (size_t)bh * N * D;
+    // (every wave is past the previous head's last tile: its closing
+    // barrier has run, so slot 0 is free)
+    load_tile(t_first * kBwdRows, 0);
+    wait_loads_and_barrier<0>();
+    int t = t_first;
+    for (; t < t_inner; ++t) tile(t, std::true_type{});
+    for (; t < t_tail; ++t) tile(t, std::false_type{});
+    for (; t < n_qtiles; ++t) tile(t, std::true_type{});
+  }
 
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds its key's d values in groups of 4
   if (key < N) {
@@ -367,11 +391,13 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   }
   {
     const int n_kblocks = (p.N + kBwdKeys - 1) / kBwdKeys;
-    const long long blocks = (long long)p.B * p.H * n_kblocks;
+    const long long blocks = (long long)p.B * p.Hkv * n_kblocks;
+    // fewer than 8 workgroups per compute unit: order the grid longest first
+    const int block_major = CAUSAL && blocks < 8 * 256;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * kBwdWaves), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, (const float*)L2vec, (const float*)Dvec, (uint16_t*)dk, (uint16_t*)dv,
-                       p.N, n_kblocks, p.scale * kLog2e, p.scale);
+                       p.N, n_kblocks, p.B * p.Hkv, block_major, p.group(), p.scale * kLog2e, p.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(64 * NW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ LSE, const float* __restrict__ Dvec,
-              uint16_t* __restrict__ dQ, int N, int n_qtiles, float c2, float scale) {
+              uint16_t* __restrict__ dQ, int N, int n_qtiles, int group, float c2, float scale) {
   using C = DqCfg<D, NW, BN, S>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -92,8 +92,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int row0 = __builtin_amdgcn_readfirstlane(q0 + 32 * w);
   const int qrow = row0 + n;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  // consecutive query heads share a key/value head: (b, h) reads (b, h / group)
+  const size_t kvhead = (size_t)__builtin_amdgcn_readfirstlane(bh / group) * N * D;
+  const uint16_t* Kh = K + kvhead;
+  const uint16_t* Vh = V + kvhead;
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
   const int n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
@@ -274,7 +276,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* dO, c
   const long long grid = (long long)p.B * p.H * n_qtiles;
   hipLaunchKernelGGL((bwd_dq_kernel<D, NW, BN, S, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (const uint16_t*)dO, lse, Dvec, (uint16_t*)dq, p.N, n_qtiles,
+                     (const uint16_t*)dO, lse, Dvec, (uint16_t*)dq, p.N, n_qtiles, p.group(),
                      p.scale * kLog2e, p.scale);
   return hipGetLastError();
 }

@@ -117,7 +117,7 @@ template <int D, int NW, int BN, int S, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int N, int n_qtiles, float c2) {
+                float* __restrict__ LSE, int N, int n_qtiles, int group, float c2) {
   using C = FwdCfg<D, NW, BN, S>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -141,9 +141,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int row0 = __builtin_amdgcn_readfirstlane(q0 + 32 * w);
   const int qrow = row0 + n;
   const size_t head = (size_t)bh * N * D;
+  // consecutive query heads share a key/value head: (b, h) reads (b, h / group)
+  const size_t kvhead = (size_t)__builtin_amdgcn_readfirstlane(bh / group) * N * D;
   const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const uint16_t* Kh = K + kvhead;
+  const uint16_t* Vh = V + kvhead;
 
   const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
   const int n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
@@ -496,7 +498,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const float c2 = p.scale * kLog2e;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, S, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     p.N, n_qtiles, c2);
+                     p.N, n_qtiles, p.group(), c2);
   return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@ struct Problem {
   int B, H, N, d;
   int causal;
   float scale;
+  int Hkv;  // key/value heads; query head h reads key/value head h / (H / Hkv)
+  int group() const { return H / Hkv; }
 };
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -34,6 +34,26 @@ CONFIGS = {
 }
 
 
+# Shared key/value heads: the causal 16K-token shape above with 32 query heads
+# over 8 key/value heads (groups of 4), and a multi-query variant (one
+# key/value head). The pages give no shared-head workload; these keep the
+# headline shape and vary only the head sharing.
+GQA_WORKLOADS = {
+    "gqa": dict(name="fwd_causal_bf16_b8h32kv8n16384d128", B=8, H=32, Hkv=8, N=16384, d=128,
+                dtype="bf16", causal=True, q_mult=1.0, seed=3811),
+    "mqa": dict(name="fwd_causal_bf16_b8h32kv1n16384d128", B=8, H=32, Hkv=1, N=16384, d=128,
+                dtype="bf16", causal=True, q_mult=1.0, seed=3812),
+}
+
+
+def gqa_config(kind):
+    c = dict(GQA_WORKLOADS[kind])
+    c["id"] = kind
+    c["scale"] = 1.0 / float(np.sqrt(c["d"]))
+    c["passes"] = ("fwd", "fwd+bwd")
+    return c
+
+
 def config(cid):
     c = dict(CONFIGS[cid])
     c["id"] = cid
@@ -45,20 +65,23 @@ def _randn(shape, gen, device):
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
 
 
-def make_inputs(cfg, device, with_do=False, shape=None, seed=None):
+def make_inputs(cfg, device, with_do=False, shape=None, seed=None, kv_heads=None):
     """Seeded (q, k, v[, do]) for a configuration dict (or an explicit shape).
 
     bf16 tensors are drawn in fp32 and rounded; config['q_mult'] multiplies q
-    after drawing (x4 is exact in bf16). Returns contiguous tensors on device.
+    after drawing (x4 is exact in bf16). k and v get `kv_heads` heads
+    (default: config['Hkv'], else as many as q). Returns contiguous tensors on
+    device.
     """
     B, H, N, d = shape or (cfg["B"], cfg["H"], cfg["N"], cfg["d"])
+    Hkv = kv_heads or cfg.get("Hkv") or H
     gen = torch.Generator(device=device)
     gen.manual_seed(cfg["seed"] if seed is None else seed)
     out_dtype = torch.float32 if cfg.get("dtype") == "f32" else torch.bfloat16
     names = ["q", "k", "v"] + (["do"] if with_do else [])
     tensors = []
     for name in names:
-        x = _randn((B, H, N, d), gen, device)
+        x = _randn((B, Hkv if name in ("k", "v") else H, N, d), gen, device)
         if name == "q" and cfg.get("q_mult", 1.0) != 1.0:
             x.mul_(cfg["q_mult"])
         tensors.append(x.to(out_dtype).contiguous())

@@ -64,7 +64,8 @@ extern "C" {
 enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
-  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or a size overflows the limits above  */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, Hkv does not divide H, or a size
+                             overflows the limits above                          */
   FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or causal not in {0, 1}          */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
   FA_ERR_SCALE = 5,       /* scale is not positive, or NaN or infinite           */
@@ -87,6 +88,22 @@ enum {
  */
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Forward with shared key/value heads (grouped-query attention; one key/value
+ * head for all query heads is multi-query attention). "Attention and KV
+ * Compression", "The composability point": sharing key/value heads changes
+ * only how many of them there are, and the tiled forward runs over them
+ * unchanged. Query head h of H reads key/value head h / (H / Hkv), so each
+ * group of H / Hkv consecutive query heads shares one; per query head the
+ * result is exactly fa_forward's on that head's K and V.
+ *   q, o : bf16 [B, H, N, d];  k, v : const bf16 [B, Hkv, N, d];  lse : fp32 [B, H, N]
+ *   Hkv  : 1 <= Hkv <= H and H % Hkv == 0, else FA_ERR_SHAPE.
+ * Everything else as fa_forward, which is this call with Hkv = H.
+ */
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Hkv, int N, int d, int causal, float scale,
+                   hipStream_t stream);
 
 /*
  * Forward, fp32 inputs, fp32 arithmetic, fp32 output; same tiling and online
@@ -126,6 +143,22 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
                 int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Backward of fa_forward_gqa. The gradient of a shared key/value head is the
+ * sum of what each query head of its group sends it (the chain rule over a
+ * shared input); the dK/dV kernel streams the query tiles of all heads of the
+ * group through one key block and sums them in registers, so dk and dv are
+ * written once, with no atomics, and stay bitwise reproducible.
+ *   q, o, dO, dq : bf16 [B, H, N, d];  k, v, dk, dv : bf16 [B, Hkv, N, d];
+ *   lse : const fp32 [B, H, N];  Hkv as fa_forward_gqa;
+ *   workspace : fa_backward_workspace_bytes(B, H, N, d) bytes (per query head).
+ * Everything else as fa_backward, which is this call with Hkv = H.
+ */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                    int B, int H, int Hkv, int N, int d, int causal, float scale,
+                    hipStream_t stream);
 
 /* Static text for a status code; for FA_ERR_LAUNCH the text of the calling
  * thread's last HIP launch error. Never NULL. */

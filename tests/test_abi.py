@@ -59,7 +59,18 @@ def test_status_strings(L):
     assert _lib.status_string(12345) == "unknown status"
 
 
-def _prevalidate(kind, ptrs, B, H, N, d, causal, scale):
+ENTRY_POINTS = ["fa_forward", "fa_forward_f32", "fa_backward", "fa_forward_gqa", "fa_backward_gqa"]
+
+
+def _is_gqa(fn):
+    return fn.endswith("_gqa")
+
+
+def _nptr(fn):
+    return 10 if fn.startswith("fa_backward") else 5
+
+
+def _prevalidate(kind, ptrs, B, H, N, d, causal, scale, Hkv=None):
     """Python restatement of the documented checks, in the documented order."""
     if any(p in (None, 0) for p in ptrs):
         return CODES["FA_ERR_NULL"]
@@ -73,69 +84,79 @@ def _prevalidate(kind, ptrs, B, H, N, d, causal, scale):
         return CODES["FA_ERR_UNSUPPORTED"]
     if not (scale > 0) or not math.isfinite(scale):
         return CODES["FA_ERR_SCALE"]
+    if Hkv is not None and (Hkv < 1 or Hkv > H or H % Hkv):
+        return CODES["FA_ERR_SHAPE"]
     if any(p % 16 for p in ptrs):
         return CODES["FA_ERR_ALIGN"]
     return OK
 
 
-def _expect(L, fn, code, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125):
-    nptr = 10 if fn == "fa_backward" else 5
-    ptrs = [A] * nptr if ptrs is None else ptrs
-    pre = _prevalidate(fn, ptrs, B, H, N, d, causal, scale)
+def _expect(L, fn, code, ptrs=None, B=1, H=1, N=16, d=64, causal=0, scale=0.125, Hkv=None):
+    ptrs = [A] * _nptr(fn) if ptrs is None else ptrs
+    if _is_gqa(fn) and Hkv is None:
+        Hkv = H
+    pre = _prevalidate(fn, ptrs, B, H, N, d, causal, scale, Hkv if _is_gqa(fn) else None)
     assert pre != OK, "refusing to call the library with arguments that would launch a kernel"
     assert pre == code, (pre, code)
-    args = [ctypes.c_void_p(p) if p else None for p in ptrs] + [B, H, N, d, causal, ctypes.c_float(scale), None]
+    heads = [B, H, Hkv] if _is_gqa(fn) else [B, H]
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs] + heads + [N, d, causal, ctypes.c_float(scale), None]
     rc = getattr(L, fn)(*args)
     assert rc == code, (fn, rc, _lib.status_string(rc))
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 def test_null_pointers(L, fn):
-    n = 10 if fn == "fa_backward" else 5
+    n = _nptr(fn)
     for i in range(n):
         ptrs = [A] * n
         ptrs[i] = 0
         _expect(L, fn, CODES["FA_ERR_NULL"], ptrs=ptrs)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 @pytest.mark.parametrize("B,H,N", [(0, 1, 16), (1, 0, 16), (1, 1, 0), (-1, 1, 16), (1, 1, -5)])
 def test_bad_shape(L, fn, B, H, N):
     _expect(L, fn, CODES["FA_ERR_SHAPE"], B=B, H=H, N=N)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 def test_size_overflow(L, fn):
     _expect(L, fn, CODES["FA_ERR_SHAPE"], B=2**30, H=2**20, N=2**20, d=128)
     _expect(L, fn, CODES["FA_ERR_SHAPE"], B=65536, H=65536, N=2**10, d=64)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 @pytest.mark.parametrize("d", [0, 1, 32, 63, 96, 127, 129, 256])
 def test_unsupported_head_dim(L, fn, d):
     _expect(L, fn, CODES["FA_ERR_UNSUPPORTED"], d=d)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 @pytest.mark.parametrize("causal", [-1, 2, 7])
 def test_bad_causal_flag(L, fn, causal):
     _expect(L, fn, CODES["FA_ERR_UNSUPPORTED"], causal=causal)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 @pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), -float("inf")])
 def test_bad_scale(L, fn, scale):
     _expect(L, fn, CODES["FA_ERR_SCALE"], scale=scale)
 
 
-@pytest.mark.parametrize("fn", ["fa_forward", "fa_forward_f32", "fa_backward"])
+@pytest.mark.parametrize("fn", ENTRY_POINTS)
 def test_misaligned_pointers(L, fn):
-    n = 10 if fn == "fa_backward" else 5
+    n = _nptr(fn)
     for i in range(n):
         for off in (2, 4, 8):
             ptrs = [A] * n
             ptrs[i] = A + off
             _expect(L, fn, CODES["FA_ERR_ALIGN"], ptrs=ptrs)
+
+
+@pytest.mark.parametrize("fn", ["fa_forward_gqa", "fa_backward_gqa"])
+@pytest.mark.parametrize("H,Hkv", [(8, 0), (8, -2), (8, 3), (8, 16), (6, 4), (1, 2)])
+def test_bad_kv_heads(L, fn, H, Hkv):
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], H=H, Hkv=Hkv)
 
 
 def test_workspace_bytes(L):
