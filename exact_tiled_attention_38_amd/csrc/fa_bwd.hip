@@ -40,6 +40,9 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdRows = 64;              // query rows per tile
 
+// The dK/dV grid walks key/value heads in chunks of this many (one per XCD).
+constexpr int kBwdHeadChunk = 8;
+
 // Q and dO tiles (kBwdRows rows) arrive by direct-to-LDS loads into a
 // two-slot ring, unpadded, with the 16-byte chunks of each row XOR-swizzled
 // so that both the 128-bit row reads (16 rows, one chunk column) and the
@@ -99,7 +102,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ L2vec, const float* __restrict__ Dvec,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                int N, int n_kblocks, int n_kvheads, int block_major, int group, float c2, float scale) {
+                int N, int n_kblocks, int n_kvheads, int group, float c2, float scale) {
   using C = BwdCfg<D>;
   // ring slot s: Q tile at qd + (2s) TILEB, dO tile at qd + (2s+1) TILEB
   __shared__ __attribute__((aligned(1024))) char qd[4 * C::TILEB];
@@ -111,19 +114,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int h = lane >> 5, n = lane & 31;
   // workgroup -> (key/value head, key block); the key/value head is shared
   // by query heads kvbh * group .. + group - 1, whose gradients it sums.
-  // Head-major by default: the key blocks of a head run side by side and
-  // share its query tiles in L2. A small grid (few key/value heads, long
-  // groups) goes key-block-major instead, so that under a causal mask the
-  // longest blocks start first and the last wave of workgroups is short.
-  int kvbh, kbi;
-  if (block_major) {
-    kbi = blockIdx.x / n_kvheads;
-    kvbh = blockIdx.x - kbi * n_kvheads;
-  } else {
-    kvbh = blockIdx.x / n_kblocks;
-    kbi = blockIdx.x - kvbh * n_kblocks;
-  }
-  kvbh = __builtin_amdgcn_readfirstlane(kvbh);
+  // The grid takes the heads in chunks of kBwdHeadChunk and, inside a chunk,
+  // goes key-block-major: workgroup b runs on XCD b % 8, so each XCD keeps
+  // to one head of the chunk and its concurrent key blocks share that head's
+  // query tiles in L2, and under a causal mask the longest key blocks (the
+  // first ones) start first, so the last workgroups to start are short.
+  const int chunk = blockIdx.x / (kBwdHeadChunk * n_kblocks);
+  const int r = blockIdx.x - chunk * (kBwdHeadChunk * n_kblocks);
+  const int cc = min(kBwdHeadChunk, n_kvheads - kBwdHeadChunk * chunk);  // heads in this chunk
+  const int kbi = r / cc;
+  const int kvbh = __builtin_amdgcn_readfirstlane(kBwdHeadChunk * chunk + r - kbi * cc);
   const int kb0 = __builtin_amdgcn_readfirstlane(kbi * kBwdKeys);
   const int kw0 = kb0 + 32 * w;
   const int key = kw0 + n;
@@ -392,12 +392,10 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   {
     const int n_kblocks = (p.N + kBwdKeys - 1) / kBwdKeys;
     const long long blocks = (long long)p.B * p.Hkv * n_kblocks;
-    // fewer than 8 workgroups per compute unit: order the grid longest first
-    const int block_major = CAUSAL && blocks < 8 * 256;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64 * kBwdWaves), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, (const float*)L2vec, (const float*)Dvec, (uint16_t*)dk, (uint16_t*)dv,
-                       p.N, n_kblocks, p.B * p.Hkv, block_major, p.group(), p.scale * kLog2e, p.scale);
+                       p.N, n_kblocks, p.B * p.Hkv, p.group(), p.scale * kLog2e, p.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
