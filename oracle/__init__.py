@@ -7,6 +7,7 @@ with it. See attention.py (the one-shot definition) and online_softmax.py
 """
 
 from .attention import backward, forward, scores, softmax_rows
+from .decode import forward_decode, forward_decode_heads, merge_partials
 from .heads import backward_heads, forward_heads, kv_head
 from .online_softmax import blockwise_forward, online_softmax_row
 
@@ -20,4 +21,7 @@ __all__ = [
     "kv_head",
     "forward_heads",
     "backward_heads",
+    "forward_decode",
+    "forward_decode_heads",
+    "merge_partials",
 ]
