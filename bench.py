@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
-    ap.add_argument("--workload", choices=["gqa", "mqa"],
+    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long"],
                     help="instead of --config: the same causal 16K shape with 8 (gqa) or 1 (mqa) "
-                         "key/value heads shared by the 32 query heads")
+                         "key/value heads shared by the 32 query heads, or a decode workload (one "
+                         "query per head against a 16K or 100K-token cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -209,6 +210,65 @@ def cpu_baseline(cfg, q, k, v, target_s):
     }
 
 
+def decode_bytes(cfg):
+    """Algorithmic bytes of one decode call: K and V read once, Q read, O and lse written."""
+    B, H, Hkv, Nq, Nk, d = (cfg[x] for x in ("B", "H", "Hkv", "Nq", "Nk", "d"))
+    return 2.0 * B * Hkv * Nk * d * 2 + 2.0 * B * H * Nq * d * 2 + 4.0 * B * H * Nq
+
+
+def bench_decode(a, cfg):
+    """One decode call (split kernel + merge kernel) per step; HBM roofline."""
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+    from exact_tiled_attention_38_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q, k, v = W.make_decode_inputs(cfg, dev)
+    B, H, Hkv, Nq, Nk, d = (cfg[x] for x in ("B", "H", "Hkv", "Nq", "Nk", "d"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(B, H, Hkv, Nq, Nk, d), dtype=torch.uint8, device=dev)
+    scale = 1.0 / d ** 0.5
+    step = lambda: fa.decode(q, k, v, causal=cfg["causal"], scale=scale, workspace=ws, out=o, lse=lse)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    ms = total_ms / a.steps
+    nbytes = decode_bytes(cfg)
+    launch_avg = sum(per) / len(per)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (launch_avg * 1e-3) / 1e9
+    return {
+        "metric": "attention decode: algorithmic HBM bytes per second (K and V read once)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"bf16 decode, B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d}"
+                               + (" causal" if cfg["causal"] else ""),
+                   "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "causal": bool(cfg["causal"])},
+        "roofline": {
+            "kernel": "decode_kernel + merge_kernel (one fa_decode call)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "launch_avg_ms": round(launch_avg, 5),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -224,6 +284,9 @@ def main():
     import exact_tiled_attention_38_amd as fa
     from exact_tiled_attention_38_amd import workloads as W
 
+    if a.workload and a.workload.startswith("decode"):
+        print(json.dumps(bench_decode(a, W.DECODE_WORKLOADS[a.workload])), flush=True)
+        return
     cfg = W.gqa_config(a.workload) if a.workload else W.config(a.config)
     B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
     Hkv = cfg.get("Hkv", H)

@@ -6,6 +6,8 @@ thin Python binding: it checks tensors, allocates outputs with PyTorch and
 passes device pointers and the current stream to the library.
 """
 
-from .api import backward, backward_workspace_bytes, forward, forward_f32, status_string
+from .api import (backward, backward_workspace_bytes, decode, decode_workspace_bytes, forward, forward_f32,
+                  merge, status_string)
 
-__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "status_string"]
+__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "decode",
+           "decode_workspace_bytes", "merge", "status_string"]

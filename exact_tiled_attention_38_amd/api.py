@@ -12,7 +12,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "status_string"]
+__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "decode",
+           "decode_workspace_bytes", "merge", "status_string"]
 
 
 def status_string(code):
@@ -137,3 +138,66 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
     )
     _lib.check(rc, "fa_backward_gqa")
     return dq, dk, dv
+
+
+def decode_workspace_bytes(B, H, Hkv, Nq, Nk, d):
+    return int(_lib.lib().fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d))
+
+
+def decode(q, k, v, causal=False, scale=None, workspace=None, out=None, lse=None):
+    """Attention of a few new queries against a cached sequence. Returns (o, lse).
+
+    q: bf16 [B, H, Nq, d], the last Nq positions of the sequence; k, v: bf16
+    [B, Hkv, Nk, d] with Hkv dividing H. causal: query i sees keys
+    j <= Nk - Nq + i. A workspace of decode_workspace_bytes() bytes is
+    allocated unless given.
+    """
+    B, H, Nq, d = _check([q], ["q"], torch.bfloat16)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k must be [B, Hkv, Nk, d] with B={B}, d={d}; got {tuple(k.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"k/v have {Hkv} heads, which must divide q's {H} heads")
+    _check([k, v], ["k", "v"], torch.bfloat16, (B, Hkv, Nk, d))
+    if k.device != q.device:
+        raise ValueError(f"k is on {k.device}, expected {q.device}")
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check([o], ["out"], torch.bfloat16, (B, H, Nq, d))
+    _check([l], ["lse"], torch.float32, (B, H, Nq))
+    nbytes = decode_workspace_bytes(B, H, Hkv, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes or workspace.device != q.device:
+        raise ValueError(f"workspace must hold {nbytes} bytes on {q.device}")
+    rc = _lib.lib().fa_decode(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), workspace.data_ptr(),
+        B, H, Hkv, Nq, Nk, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_decode")
+    return o, l
+
+
+def merge(o_parts, lse_parts):
+    """Merge partial results over disjoint key sets. Returns (o, lse).
+
+    o_parts: bf16 [S, *rows_shape, d]; lse_parts: fp32 [S, *rows_shape] (natural
+    log, as forward() returns it). o has shape [*rows_shape, d], lse [*rows_shape].
+    """
+    if o_parts.dim() < 3:
+        raise ValueError("o_parts must be [S, ..., d]")
+    S, d = o_parts.shape[0], o_parts.shape[-1]
+    rows_shape = tuple(o_parts.shape[1:-1])
+    _check([o_parts], ["o_parts"], torch.bfloat16, tuple(o_parts.shape))
+    _check([lse_parts], ["lse_parts"], torch.float32, (S,) + rows_shape)
+    if lse_parts.device != o_parts.device:
+        raise ValueError(f"lse_parts is on {lse_parts.device}, expected {o_parts.device}")
+    rows = 1
+    for x in rows_shape:
+        rows *= x
+    o = torch.empty(rows_shape + (d,), dtype=torch.bfloat16, device=o_parts.device)
+    l = torch.empty(rows_shape, dtype=torch.float32, device=o_parts.device)
+    rc = _lib.lib().fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), o.data_ptr(), l.data_ptr(),
+                             S, rows, d, _stream(o_parts))
+    _lib.check(rc, "fa_merge")
+    return o, l

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip"]
 # The bf16 forward's row max runs on v_max_f32 without the IEEE-mode NaN
 # quieting that fmaxf otherwise needs (an extra canonicalising op per score):
 # the kernels never see NaN scores from finite inputs.

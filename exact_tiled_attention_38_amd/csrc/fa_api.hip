@@ -14,16 +14,26 @@ thread_local char g_launch_error[256] = "kernel launch failed";
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Sizes shared by every entry point. Returns FA_OK or the first failing code.
+constexpr long double k2p62 = 4.611686018427387904e18L;
+
+// A launch covers fewer than 2^32 work-items in its (one-dimensional) grid.
+bool fits_grid(long double blocks, int threads) { return blocks * threads < 4294967296.0L; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Sizes shared by the forward and backward entry points: element counts
+// below 2^62 and every kernel grid in range (256-row bf16 forward and dQ
+// blocks of 512 threads, 64-row fp32 forward blocks of 64 threads, 128-key
+// dK/dV blocks of 256 threads, one thread per 8 values in the backward's row
+// preprocessing). Returns FA_OK or the first failing code.
 int check_sizes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const long double elems = (long double)B * H * N * d;
-  if (elems >= 4.611686018427387904e18L) return FA_ERR_SHAPE;  // 2^62
-  const long long rows_blocks = ((long long)N + fa::kFwdRowsPerBlock - 1) / fa::kFwdRowsPerBlock;
-  if ((long double)B * H * (long double)rows_blocks >= 2147483648.0L) return FA_ERR_SHAPE;
-  // the f32 path uses 64-row blocks
-  if ((long double)B * H * (long double)(((long long)N + 63) / 64) >= 2147483648.0L) return FA_ERR_SHAPE;
+  const long double bh = (long double)B * H;
+  if (bh * N * d >= k2p62) return FA_ERR_SHAPE;
+  if (!fits_grid(bh * ceil_div(N, fa::kFwdRowsPerBlock), 512) || !fits_grid(bh * ceil_div(N, 64), 64) ||
+      !fits_grid(bh * ceil_div(N, 128), 256) || !fits_grid(bh * N * (d / 8), 1))
+    return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -38,6 +48,25 @@ int check_common(int B, int H, int N, int d, int causal, float scale) {
 // Key/value heads: 1 <= Hkv <= H and Hkv divides H.
 int check_kv_heads(int H, int Hkv) {
   if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Decode sizes: heads as fa_forward_gqa, Nq queries at the end of Nk keys.
+int check_decode(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (check_kv_heads(H, Hkv) != FA_OK) return FA_ERR_SHAPE;
+  if (Nk >= (1 << 24)) return FA_ERR_SHAPE;  // 32-bit byte offsets within a key split
+  if ((long double)B * H * Nq * d >= k2p62) return FA_ERR_SHAPE;
+  if ((long double)B * Hkv * Nk * d >= k2p62) return FA_ERR_SHAPE;
+  // grids: at most ceil(Nk / 64) splits per 32-row query block, up to 256
+  // threads per workgroup; the merge takes up to 256 threads per output row
+  const long long R = (long long)(H / Hkv) * Nq;
+  if (!fits_grid((long double)B * Hkv * ceil_div(R, 32) * ceil_div(Nk, 64), 256)) return FA_ERR_SHAPE;
+  if (!fits_grid((long double)B * H * Nq, 256)) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FA_ERR_SCALE;
   return FA_OK;
 }
 
@@ -103,6 +132,33 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 int N, int d, int causal, float scale, hipStream_t stream) {
   return fa_backward_gqa(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, H, H, N, d, causal, scale,
                          stream);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  if (check_decode(B, H, Hkv, Nq, Nk, d, 0, 1.f) != FA_OK) return 0;
+  return fa::decode_workspace_bytes(fa::DecodeProblem{B, H, Hkv, Nq, Nk, d, 0, 1.f});
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int B,
+              int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  const int s = check_decode(B, H, Hkv, Nq, Nk, d, causal, scale);
+  if (s != FA_OK) return s;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const fa::DecodeProblem p{B, H, Hkv, Nq, Nk, d, causal, scale};
+  return launch_status(fa::launch_decode(q, k, v, o, lse, workspace, p, stream));
+}
+
+int fa_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int S, long long rows,
+             int d, hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (S < 1 || rows < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((long double)S * rows * d >= k2p62 || !fits_grid((long double)rows, 256)) return FA_ERR_SHAPE;
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  return launch_status(fa::launch_merge_bf16(o_parts, lse_parts, o, lse, S, rows, d, stream));
 }
 
 const char* fa_status_string(int status) {

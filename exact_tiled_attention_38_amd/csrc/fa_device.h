@@ -114,4 +114,19 @@ __device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
   return __builtin_convertvector(f, bf16x2_t);
 }
 
+// Chunk swizzles (XOR on the 16-byte chunk index within a row). RPL = rows
+// per 256-byte bank line. K: the 16 rows of one 128-bit read phase land on 16
+// distinct chunk slots. V: the 4 rows of one transposed read phase land in 4
+// distinct 64-byte quarters of the bank line.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  constexpr int RPL = 128 / D;
+  return (r / RPL) & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int RPL = 128 / D;
+  return 4 * ((r / RPL) & (4 / RPL - 1));
+}
+
 }  // namespace fa

@@ -98,21 +98,6 @@ struct FwdCfg {
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
 };
 
-// Chunk swizzles (XOR on the 16-byte chunk index within a row). RPL = rows
-// per 256-byte bank line. K: the 16 rows of one 128-bit read phase land on 16
-// distinct chunk slots. V: the 4 rows of one transposed read phase land in 4
-// distinct 64-byte quarters of the bank line.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  constexpr int RPL = 128 / D;
-  return (r / RPL) & (D / 8 - 1);
-}
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-  constexpr int RPL = 128 / D;
-  return 4 * ((r / RPL) & (4 / RPL - 1));
-}
-
 template <int D, int NW, int BN, int S, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,

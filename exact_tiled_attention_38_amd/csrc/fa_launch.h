@@ -34,4 +34,30 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 // Query rows per workgroup of the bf16 forward (sets the grid-size limit).
 constexpr int kFwdRowsPerBlock = 256;
 
+// Decode: Nq queries per head at the end of a sequence of Nk keys.
+struct DecodeProblem {
+  int B, H, Hkv, Nq, Nk, d;
+  int causal;
+  float scale;
+};
+// How the decode kernel splits its work (a function of the sizes only).
+struct DecodePlan {
+  int R;          // query rows per key/value head: (H / Hkv) * Nq
+  int n_rblocks;  // blocks of 32 of those rows
+  int S;          // key splits
+  int L;          // keys per split (the last may hold fewer)
+  long long P;    // padded partial rows per split: B * Hkv * n_rblocks * 32
+};
+#ifndef FA_DEC_WAVES
+#define FA_DEC_WAVES 2
+#endif
+constexpr int kDecodeWaves = FA_DEC_WAVES;
+DecodePlan decode_plan(const DecodeProblem& p);
+size_t decode_workspace_bytes(const DecodeProblem& p);
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                         const DecodeProblem& p, hipStream_t stream);
+// Merge of S bf16 partial outputs [S][rows][d] with their lse [S][rows].
+hipError_t launch_merge_bf16(const void* o_parts, const float* lse_parts, void* o, float* lse, int S,
+                             long long rows, int d, hipStream_t stream);
+
 }  // namespace fa

@@ -46,6 +46,34 @@ GQA_WORKLOADS = {
 }
 
 
+# Decode: one new query per head against a cached sequence. The first two
+# keep the headline shape (batch 8, 32 query heads, 16K cached tokens,
+# d = 128) with 32 or 8 key/value heads; the third is the 100,000-token
+# single-sequence length of the long-context page with 8 heads. Queries sit
+# at the end of the sequence (causal; with one query that masks nothing).
+DECODE_WORKLOADS = {
+    "decode": dict(name="decode_bf16_b8h32kv32nq1nk16384d128", B=8, H=32, Hkv=32, Nq=1, Nk=16384, d=128,
+                   causal=True, seed=3821),
+    "decode_gqa": dict(name="decode_bf16_b8h32kv8nq1nk16384d128", B=8, H=32, Hkv=8, Nq=1, Nk=16384, d=128,
+                       causal=True, seed=3822),
+    "decode_long": dict(name="decode_bf16_b1h8kv8nq1nk100000d128", B=1, H=8, Hkv=8, Nq=1, Nk=100000, d=128,
+                        causal=True, seed=3823),
+}
+
+
+def make_decode_inputs(cfg, device):
+    """Seeded bf16 q [B, H, Nq, d] and k, v [B, Hkv, Nk, d], i.i.d. N(0, 1)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg["seed"])
+    out = []
+    for shape in ((cfg["B"], cfg["H"], cfg["Nq"], cfg["d"]), (cfg["B"], cfg["Hkv"], cfg["Nk"], cfg["d"]),
+                  (cfg["B"], cfg["Hkv"], cfg["Nk"], cfg["d"])):
+        x = _randn(shape, gen, device)
+        out.append(x.to(torch.bfloat16).contiguous())
+        del x
+    return tuple(out)
+
+
 def gqa_config(kind):
     c = dict(GQA_WORKLOADS[kind])
     c["id"] = kind

@@ -46,7 +46,9 @@
  *     fa_status_string() then includes the HIP error text (per thread).
  *     Faults during execution surface at the caller's next synchronization.
  *   - Supported: B, H, N >= 1; d in {64, 128}; causal in {0, 1};
- *     0 < scale < inf; B*H*N*d < 2^62 and B*H*ceil(N/64) < 2^31.
+ *     0 < scale < inf; B*H*N*d < 2^62, and every kernel grid below 2^32
+ *     work-items: B*H*ceil(N/256)*512, B*H*ceil(N/64)*64 and B*H*N*d/8
+ *     each < 2^32 (at N = 16384, d = 128: B*H < 16384).
  *   - Thread safety: stateless apart from a per-thread error string.
  *   - Determinism: forward and backward outputs are bitwise reproducible run
  *     to run (no atomics anywhere).
@@ -159,6 +161,51 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
                     int B, int H, int Hkv, int N, int d, int causal, float scale,
                     hipStream_t stream);
+
+/*
+ * Decode: Nq new queries per head (typically 1, or a few) against a cached
+ * sequence of Nk keys, the workload that "FlashAttention — how 100K-token
+ * attention fits in memory", "Arithmetic intensity", sets against prefill:
+ * the same exact attention, bound by reading K and V once. The queries are
+ * the last Nq positions of the sequence; with causal = 1 query i sees keys
+ * j <= Nk - Nq + i (with Nq = 1 every key; Nq = Nk is fa_forward's mask).
+ * Key/value heads may be shared as in fa_forward_gqa.
+ * The keys of each head are split across workgroups; each split writes a
+ * partial (O_s, lse_s) into the workspace and a second kernel merges them
+ * by the rescale identity of online softmax ("Online softmax intuition";
+ * "Attention and KV Compression", "Tiling and online softmax"), as fa_merge
+ * does.
+ *   q, o      : bf16 [B, H, Nq, d];  k, v : const bf16 [B, Hkv, Nk, d] (the cache)
+ *   lse       : fp32 [B, H, Nq] (output, natural log)
+ *   workspace : fa_decode_workspace_bytes(...) bytes of device memory,
+ *               16-byte aligned; contents on entry do not matter.
+ * Limits: Nk < 2^24; B*Hkv*ceil(H/Hkv*Nq/32)*ceil(Nk/64)*256 < 2^32 and
+ * B*H*Nq*256 < 2^32; causal requires Nq <= Nk (else FA_ERR_SHAPE). The
+ * split count is a function of the sizes only, so results are bitwise
+ * reproducible. Two calls may not share a workspace concurrently.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+              int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              hipStream_t stream);
+
+/*
+ * Merge S partial attention results computed over disjoint sets of keys
+ * into the result over their union ("Online softmax intuition": the rescale
+ * that lets blockwise processing reach the exact softmax), for example the
+ * outputs of fa_forward on key shards (non-causal) held by different
+ * devices:
+ *     M = max_s lse_s,  lse = M + ln sum_s e^(lse_s - M),
+ *     o = sum_s e^(lse_s - lse) o_s.
+ * A part with lse_s = -inf (no visible key) weighs nothing; a row whose
+ * parts are all -inf gets o = 0 and lse = -inf.
+ *   o_parts   : const bf16 [S, rows, d]  (part s is a [rows, d] block)
+ *   lse_parts : const fp32 [S, rows]     (natural log, as fa_forward writes it)
+ *   o         : bf16 [rows, d];  lse : fp32 [rows]  (outputs)
+ * S >= 1, 1 <= rows < 2^24, S*rows*d < 2^62, d in {64, 128}.
+ */
+int fa_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int S,
+             long long rows, int d, hipStream_t stream);
 
 /* Static text for a status code; for FA_ERR_LAUNCH the text of the calling
  * thread's last HIP launch error. Never NULL. */

@@ -78,7 +78,9 @@ def _prevalidate(kind, ptrs, B, H, N, d, causal, scale, Hkv=None):
         return CODES["FA_ERR_SHAPE"]
     if d not in (64, 128):
         return CODES["FA_ERR_UNSUPPORTED"]
-    if B * H * N * d >= 2**62 or B * H * -(-N // 64) >= 2**31:
+    cdiv = lambda a, b: -(-a // b)
+    if (B * H * N * d >= 2**62 or B * H * cdiv(N, 256) * 512 >= 2**32 or B * H * cdiv(N, 64) * 64 >= 2**32
+            or B * H * cdiv(N, 128) * 256 >= 2**32 or B * H * N * (d // 8) >= 2**32):
         return CODES["FA_ERR_SHAPE"]
     if causal not in (0, 1):
         return CODES["FA_ERR_UNSUPPORTED"]
@@ -123,6 +125,11 @@ def test_bad_shape(L, fn, B, H, N):
 def test_size_overflow(L, fn):
     _expect(L, fn, CODES["FA_ERR_SHAPE"], B=2**30, H=2**20, N=2**20, d=128)
     _expect(L, fn, CODES["FA_ERR_SHAPE"], B=65536, H=65536, N=2**10, d=64)
+    # just past a kernel grid's 2^32 work-items: the backward's row
+    # preprocessing at B*H = 16384, N = 16384, d = 128; the forward's
+    # 256-row blocks at N = 1 and B*H = 2^23
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], B=128, H=128, N=16384, d=128)
+    _expect(L, fn, CODES["FA_ERR_SHAPE"], B=2**12, H=2**11, N=1, d=64)
 
 
 @pytest.mark.parametrize("fn", ENTRY_POINTS)
@@ -184,3 +191,63 @@ def test_binding_raises_without_gpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.forward(x, x, x)
+
+
+# ---------------------------------------------------------------- decode / merge
+
+def _decode_call(L, ptrs=None, B=1, H=4, Hkv=4, Nq=1, Nk=64, d=64, causal=0, scale=0.125):
+    ptrs = [A] * 6 if ptrs is None else ptrs
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    return L.fa_decode(*args, B, H, Hkv, Nq, Nk, d, causal, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=[0, A, A, A, A, A]), "FA_ERR_NULL"),
+    (dict(ptrs=[A, A, A, A, A, 0]), "FA_ERR_NULL"),
+    (dict(B=0), "FA_ERR_SHAPE"),
+    (dict(H=0), "FA_ERR_SHAPE"),
+    (dict(Nq=0), "FA_ERR_SHAPE"),
+    (dict(Nk=0), "FA_ERR_SHAPE"),
+    (dict(Hkv=3), "FA_ERR_SHAPE"),
+    (dict(Hkv=8), "FA_ERR_SHAPE"),
+    (dict(Hkv=0), "FA_ERR_SHAPE"),
+    (dict(Nk=1 << 24), "FA_ERR_SHAPE"),
+    (dict(B=1 << 16, H=1 << 12, Hkv=1 << 12), "FA_ERR_SHAPE"),
+    (dict(causal=1, Nq=65, Nk=64), "FA_ERR_SHAPE"),
+    (dict(d=96), "FA_ERR_UNSUPPORTED"),
+    (dict(causal=2), "FA_ERR_UNSUPPORTED"),
+    (dict(scale=0.0), "FA_ERR_SCALE"),
+    (dict(scale=float("nan")), "FA_ERR_SCALE"),
+    (dict(ptrs=[A, A, A, A + 8, A, A]), "FA_ERR_ALIGN"),
+    (dict(ptrs=[A, A, A, A, A, A + 4]), "FA_ERR_ALIGN"),
+])
+def test_decode_rejects_invalid_arguments(L, kw, code):
+    assert _decode_call(L, **kw) == CODES[code]
+
+
+def test_decode_workspace_bytes(L):
+    f = L.fa_decode_workspace_bytes
+    for B, H, Hkv, Nq, Nk, d in [(8, 32, 32, 1, 16384, 128), (8, 32, 8, 1, 16384, 128), (1, 8, 8, 1, 100000, 128),
+                                 (2, 32, 1, 3, 777, 64), (1, 1, 1, 1, 1, 64)]:
+        nbytes = f(B, H, Hkv, Nq, Nk, d)
+        rows_padded = B * Hkv * -(-(H // Hkv * Nq) // 32) * 32
+        assert nbytes > 0 and nbytes % ((d + 1) * 4 * rows_padded) == 0, (B, H, Hkv, Nq, Nk, d, nbytes)
+        assert nbytes // ((d + 1) * 4 * rows_padded) <= -(-Nk // 64)  # at most one split per 64 keys
+    for args in [(0, 1, 1, 1, 1, 64), (1, 6, 4, 1, 16, 64), (1, 1, 1, 1, 16, 96), (1, 1, 1, 0, 16, 64)]:
+        assert f(*args) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=[0, A, A, A]), "FA_ERR_NULL"),
+    (dict(ptrs=[A, A, A, 0]), "FA_ERR_NULL"),
+    (dict(S=0), "FA_ERR_SHAPE"),
+    (dict(rows=0), "FA_ERR_SHAPE"),
+    (dict(rows=1 << 24), "FA_ERR_SHAPE"),
+    (dict(d=32), "FA_ERR_UNSUPPORTED"),
+    (dict(ptrs=[A + 2, A, A, A]), "FA_ERR_ALIGN"),
+])
+def test_merge_rejects_invalid_arguments(L, kw, code):
+    ptrs = kw.get("ptrs", [A] * 4)
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    rc = L.fa_merge(*args, kw.get("S", 2), kw.get("rows", 10), kw.get("d", 64), None)
+    assert rc == CODES[code]
