@@ -44,6 +44,13 @@
 //     the same steps shifted by half a tile (PV of the previous tile first),
 //     so one wave of a SIMD feeds the matrix core while the other runs its
 //     exponentials.
+//   * The reference maximum of each row is lazy: it moves (and the
+//     accumulator is rescaled, in a branch taken by the whole wave) only when
+//     a score of the wave's rows exceeds its row's reference by more than
+//     2^8. With one reference per row used for P, l, acc and lse alike the
+//     result is the same exact softmax; P stays <= 2^8, far inside fp32 and
+//     bf16 range, and the per-tile rescale of the accumulator disappears
+//     from almost every step.
 //   * Every wave runs every tile of the workgroup's key range: a tile wholly
 //     after a wave's rows is masked entirely (alpha = 1, P = 0, acc and l
 //     unchanged), which keeps the loop free of branches around the work.
@@ -63,15 +70,20 @@
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 4
 #endif
-// Tuning switches (all settings compute the same result):
+// Tuning switches (all settings compute the same result up to rounding):
 // 1: the accumulator rescale is spread over the score/softmax slices (always
-// done); 0: it is a separate block skipped when no row's maximum rose
+// done); 0: it is a separate block skipped when no row's reference moved
 #ifndef FA_FWD_RESCALE_IN_SLICES
-#define FA_FWD_RESCALE_IN_SLICES 1
+#define FA_FWD_RESCALE_IN_SLICES 0
 #endif
 // 1: the upper half of the workgroup runs its steps half a tile shifted
 #ifndef FA_FWD_PINGPONG
 #define FA_FWD_PINGPONG 1
+#endif
+// > 0: the reference maximum of a row only moves when some row of the wave
+// sees a score above its reference by more than this (log2 units)
+#ifndef FA_FWD_LAZY_TAU
+#define FA_FWD_LAZY_TAU 8
 #endif
 
 namespace fa {
@@ -198,7 +210,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int voff0 = tr_row * C::ROWB + 16 * (tr_chunk ^ vswz<D>(tr_row)) + 8 * (lane & 1);
 
-  float m_run = -INFINITY;  // running max of s2 for row qrow
+  float m_run = -INFINITY;  // reference maximum of s2 for row qrow (see step_head)
   float l_run = 0.f;        // running sum of 2^(s2 - m_run) over this lane's keys
   f32x16_t acc[D / 32];     // O^T block: lane holds O[qrow][32j + 8(i/4) + 4h + i%4]
 #pragma unroll
@@ -410,7 +422,16 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     vb0 = v_addr(v_tile & (S - 1));
     asm volatile("" : "+v"(kb0), "+v"(vb0));
     const float mx = row_max(s_cur);
+#if FA_FWD_LAZY_TAU > 0
+    // Exactness does not need the true running maximum, only one reference
+    // per row used consistently for P, l and acc (and lse at the end); a
+    // stale one is kept until a score exceeds it by more than 2^TAU, so P <=
+    // 2^TAU and the accumulator rescale is skipped on almost every tile.
+    const bool move = __builtin_amdgcn_ballot_w64(mx * c2 > m_run + (float)FA_FWD_LAZY_TAU) != 0;
+    const float m_new = move ? fmaxf(m_run, mx * c2) : m_run;
+#else
     const float m_new = fmaxf(m_run, mx * c2);
+#endif
     m_use = (m_new == -INFINITY) ? 0.f : m_new;
     alpha = exp2_fast(m_run - m_use);
     m_run = m_new;
