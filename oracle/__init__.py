@@ -10,6 +10,7 @@ from .attention import backward, forward, scores, softmax_rows
 from .decode import forward_decode, forward_decode_heads, merge_partials
 from .heads import backward_heads, forward_heads, kv_head
 from .online_softmax import blockwise_forward, online_softmax_row
+from .sparse import block_mask, forward_block_sparse
 
 __all__ = [
     "forward",
@@ -24,4 +25,6 @@ __all__ = [
     "forward_decode",
     "forward_decode_heads",
     "merge_partials",
+    "block_mask",
+    "forward_block_sparse",
 ]
