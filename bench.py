@@ -42,10 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
-    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long"],
+    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long", "sparse"],
                     help="instead of --config: the same causal 16K shape with 8 (gqa) or 1 (mqa) "
                          "key/value heads shared by the 32 query heads, or a decode workload (one "
-                         "query per head against a 16K or 100K-token cache)")
+                         "query per head against a 16K or 100K-token cache), or the block-sparse "
+                         "forward on the causal 16K shape (first block + diagonal + 1/8 of the rest)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -269,6 +270,60 @@ def bench_decode(a, cfg):
     }
 
 
+def bench_sparse(a, cfg):
+    """Block-sparse forward on a seeded selection; MFMA roofline over the kept pairs."""
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+    from exact_tiled_attention_38_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    q, k, v = W.make_inputs(cfg, dev)
+    rp, cols = W.sparse_selection(B, H, N, cfg["seed"], cfg["keep"])
+    pairs = W.sparse_visible_pairs(N, rp, cols, B * H, cfg["causal"])
+    row_ptr = torch.tensor(rp, dtype=torch.int32, device=dev)
+    cols_t = torch.tensor(cols, dtype=torch.int32, device=dev)
+    scale = 1.0 / d ** 0.5
+    step = lambda: fa.forward_block_sparse(q, k, v, row_ptr, cols_t, causal=cfg["causal"], scale=scale)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    ms = total_ms / a.steps
+    flops = 4.0 * d * pairs
+    launch_avg = sum(per) / len(per)
+    dense = attention_flops(B, H, N, d, cfg["causal"])
+    return {
+        "metric": "block-sparse attention forward TFLOP/s over the kept (query, key) pairs",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"causal bf16 block-sparse attention forward, B={B} H={H} N={N} d={d}, "
+                               f"blocks 256x64: first + diagonal + {cfg['keep']} of the rest",
+                   "B": B, "H": H, "N": N, "d": d, "causal": bool(cfg["causal"]),
+                   "nnz_blocks": int(cols.shape[0]), "kept_fraction_of_causal": round(flops / dense, 4)},
+        "roofline": {
+            "kernel": "fwd_bf16_kernel (block-sparse instance)",
+            "bound": "mfma",
+            "achieved": round(flops / (launch_avg * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / (launch_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launch_avg_ms": round(launch_avg, 4),
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -286,6 +341,9 @@ def main():
 
     if a.workload and a.workload.startswith("decode"):
         print(json.dumps(bench_decode(a, W.DECODE_WORKLOADS[a.workload])), flush=True)
+        return
+    if a.workload == "sparse":
+        print(json.dumps(bench_sparse(a, W.SPARSE_WORKLOADS["sparse"])), flush=True)
         return
     cfg = W.gqa_config(a.workload) if a.workload else W.config(a.config)
     B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]

@@ -6,8 +6,8 @@ thin Python binding: it checks tensors, allocates outputs with PyTorch and
 passes device pointers and the current stream to the library.
 """
 
-from .api import (backward, backward_workspace_bytes, decode, decode_workspace_bytes, forward, forward_f32,
-                  merge, status_string)
+from .api import (SPARSE_BLOCK_M, SPARSE_BLOCK_N, backward, backward_workspace_bytes, decode,
+                  decode_workspace_bytes, forward, forward_block_sparse, forward_f32, merge, status_string)
 
-__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "decode",
-           "decode_workspace_bytes", "merge", "status_string"]
+__all__ = ["forward", "forward_f32", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
+           "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]

@@ -12,8 +12,12 @@ import torch
 
 from . import _lib
 
-__all__ = ["forward", "forward_f32", "backward", "backward_workspace_bytes", "decode",
-           "decode_workspace_bytes", "merge", "status_string"]
+__all__ = ["forward", "forward_f32", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
+           "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]
+
+# Block sizes of the block-sparse selection (FA_SPARSE_BLOCK_M / _N in include/fa.h).
+SPARSE_BLOCK_M = 256
+SPARSE_BLOCK_N = 64
 
 
 def status_string(code):
@@ -200,4 +204,34 @@ def merge(o_parts, lse_parts):
     rc = _lib.lib().fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), o.data_ptr(), l.data_ptr(),
                              S, rows, d, _stream(o_parts))
     _lib.check(rc, "fa_merge")
+    return o, l
+
+
+def forward_block_sparse(q, k, v, row_ptr, cols, causal=False, scale=None):
+    """Attention restricted to selected (query block, key block) pairs. Returns (o, lse).
+
+    q: bf16 [B, H, N, d]; k, v: bf16 [B, Hkv, N, d]. The selection is in
+    compressed-row form over the B * H * ceil(N / SPARSE_BLOCK_M) query blocks
+    (b-major, then h, then block): row_ptr int32 [rows + 1] and cols int32 [nnz]
+    key-block indices (blocks of SPARSE_BLOCK_N keys), both on q's device.
+    Rows that see no key get o = 0 and lse = -inf.
+    """
+    B, H, Hkv, N, d = _kv_heads(q, k, v)
+    n_rows = B * H * -(-N // SPARSE_BLOCK_M)
+    for t, name in ((row_ptr, "row_ptr"), (cols, "cols")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous 1-D int32 tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, expected {q.device}")
+    if row_ptr.numel() != n_rows + 1:
+        raise ValueError(f"row_ptr must have {n_rows + 1} entries, got {row_ptr.numel()}")
+    nnz = cols.numel()
+    cols_arg = cols if nnz > 0 else row_ptr  # any valid device pointer when the list is empty
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.lib().fa_forward_block_sparse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), row_ptr.data_ptr(),
+        cols_arg.data_ptr(), nnz, B, H, Hkv, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_forward_block_sparse")
     return o, l

@@ -8,6 +8,9 @@
 #include "fa.h"
 #include "fa_launch.h"
 
+static_assert(FA_SPARSE_BLOCK_M == fa::kSparseBlockM && FA_SPARSE_BLOCK_N == fa::kSparseBlockN,
+              "block-sparse block sizes of the header and the kernels");
+
 namespace {
 
 thread_local char g_launch_error[256] = "kernel launch failed";
@@ -90,6 +93,21 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
     return FA_ERR_ALIGN;
   const fa::Problem p{B, H, N, d, causal, scale, Hkv};
   return launch_status(fa::launch_fwd_bf16(q, k, v, o, lse, p, stream));
+}
+
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* row_ptr, const int* cols, int nnz, int B, int H, int Hkv, int N, int d,
+                            int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !row_ptr || !cols) return FA_ERR_NULL;
+  int s = check_common(B, H, N, d, causal, scale);
+  if (s == FA_OK) s = check_kv_heads(H, Hkv);
+  if (s == FA_OK && nnz < 0) s = FA_ERR_SHAPE;
+  if (s != FA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(row_ptr) & 3u) || (reinterpret_cast<uintptr_t>(cols) & 3u)) return FA_ERR_ALIGN;
+  const fa::Problem p{B, H, N, d, causal, scale, Hkv};
+  return launch_status(fa::launch_fwd_bf16_block_sparse(q, k, v, o, lse, row_ptr, cols, nnz, p, stream));
 }
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

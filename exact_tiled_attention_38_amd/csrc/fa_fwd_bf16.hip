@@ -110,11 +110,22 @@ struct FwdCfg {
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
 };
 
-template <int D, int NW, int BN, int S, bool CAUSAL>
+// Key-block selection of the block-sparse forward, in compressed-row form:
+// the key blocks (of BN keys) of query block r (of BM rows; r counts over
+// (b, h, block)) are cols[row_ptr[r] .. row_ptr[r + 1]). Offsets and block
+// indices are clamped into range, so no list content can send a load out of
+// bounds.
+struct BlockList {
+  const int* row_ptr;
+  const int* cols;
+  int nnz;
+};
+
+template <int D, int NW, int BN, int S, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int N, int n_qtiles, int group, float c2) {
+                float* __restrict__ LSE, int N, int n_qtiles, int group, float c2, BlockList sel) {
   using C = FwdCfg<D, NW, BN, S>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -144,8 +155,41 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* Kh = K + kvhead;
   const uint16_t* Vh = V + kvhead;
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+  // Key tiles: dense, tiles 0 .. n_tiles-1 (causal: up to the block's last
+  // row); block-sparse, the listed key blocks in list order (the online
+  // softmax does not depend on the order).
+  int n_tiles, sel_base = 0;
+  if constexpr (SPARSE) {
+    const int r = bh * n_qtiles + t;
+    const int beg = min(max(sel.row_ptr[r], 0), sel.nnz);
+    const int end = min(max(sel.row_ptr[r + 1], beg), sel.nnz);
+    sel_base = __builtin_amdgcn_readfirstlane(beg);
+    n_tiles = __builtin_amdgcn_readfirstlane(end - beg);
+  } else {
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
+  }
+  // first key of tile t (tiles past the last repeat the last one)
+  auto tile_key = [&](int t) {
+    const int tt = min(t, n_tiles - 1);
+    if constexpr (SPARSE) {
+      const int kb = min(max(sel.cols[sel_base + tt], 0), (N - 1) / BN);
+      return __builtin_amdgcn_readfirstlane(kb * BN);
+    } else {
+      return tt * BN;
+    }
+  };
+  if constexpr (SPARSE) {
+    if (n_tiles == 0) {  // nothing selected: no key is visible to these rows
+      if (qrow < N) {
+        uint16_t* Orow = O + head + (size_t)qrow * D;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) *(u32x2_t*)(Orow + 8 * c + 4 * h) = u32x2_t{0u, 0u};
+        if (h == 0) LSE[(size_t)bh * N + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   // ---- direct-to-LDS tile loads. Lane `lane` of wave-wide load i fills the
   // 16-byte LDS slot `lane` of 1 KB block w * NDMA + i of the tile buffer:
@@ -170,7 +214,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // of loads and the wait count below is a constant.
   auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA]) {
     const int slot = slot0 + (t & (S - 1));
-    const int k0 = min(t, n_tiles - 1) * BN;
+    const int k0 = tile_key(t);
     const char* base = (const char*)(src + (size_t)k0 * D);
     FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024;
     if (k0 + BN <= N) {
@@ -416,8 +460,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                   float& m_use, float& alpha) {
     load_v(u + S - 2);
     load_k(u + S);
-    const int k0 = u * BN;
-    if ((CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
+    if constexpr (SPARSE) {
+      // the even-count padding step (u = n_tiles) is masked entirely
+      const int k0 = u < n_tiles ? tile_key(u) : N;
+      if (k0 >= N || (CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
+    } else {
+      const int k0 = u * BN;
+      if ((CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
+    }
     kb0 = k_addr((u + 1) & (S - 1));
     vb0 = v_addr(v_tile & (S - 1));
     asm volatile("" : "+v"(kb0), "+v"(vb0));
@@ -480,7 +530,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l)
   if (qrow < N) {
     const float l_tot = halves_sum(l_run);
-    const float inv = 1.f / l_tot;
+    // (block-sparse rows may see no key at all: O = 0, lse = -inf)
+    const float inv = (!SPARSE || l_tot > 0.f) ? 1.f / l_tot : 0.f;
     uint16_t* Orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j)
@@ -491,20 +542,21 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         u32x2_t packed = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, bb)};
         *(u32x2_t*)(Orow + 32 * j + 8 * g + 4 * h) = packed;
       }
-    if (h == 0) LSE[(size_t)bh * N + qrow] = (m_run + log2_fast(l_tot)) * kLn2;
+    if (h == 0)
+      LSE[(size_t)bh * N + qrow] = (!SPARSE || l_tot > 0.f) ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, int NW, int BN, int S, bool CAUSAL>
+template <int D, int NW, int BN, int S, bool CAUSAL, bool SPARSE = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse,
-                  const Problem& p, hipStream_t stream) {
+                  const Problem& p, hipStream_t stream, BlockList sel = BlockList{nullptr, nullptr, 0}) {
   using C = FwdCfg<D, NW, BN, S>;
   const int n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.B * p.H * n_qtiles;
   const float c2 = p.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, S, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     p.N, n_qtiles, p.group(), c2);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, S, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
+                     p.N, n_qtiles, p.group(), c2, sel);
   return hipGetLastError();
 }
 
@@ -519,6 +571,19 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                     : launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, false>(q, k, v, o, lse, p, stream);
   return p.causal ? launch<64, 8, 64, 4, true>(q, k, v, o, lse, p, stream)
                   : launch<64, 8, 64, 4, false>(q, k, v, o, lse, p, stream);
+}
+
+hipError_t launch_fwd_bf16_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int* row_ptr, const int* cols, int nnz, const Problem& p,
+                                        hipStream_t stream) {
+  static_assert(FA_FWD_BN == kSparseBlockN && FwdCfg<128, 8, FA_FWD_BN, FA_FWD_STAGES>::BM == kSparseBlockM,
+                "the block-sparse selection is in units of the forward's tiles");
+  const BlockList sel{row_ptr, cols, nnz};
+  if (p.d == 128)
+    return p.causal ? launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, true, true>(q, k, v, o, lse, p, stream, sel)
+                    : launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, false, true>(q, k, v, o, lse, p, stream, sel);
+  return p.causal ? launch<64, 8, 64, 4, true, true>(q, k, v, o, lse, p, stream, sel)
+                  : launch<64, 8, 64, 4, false, true>(q, k, v, o, lse, p, stream, sel);
 }
 
 }  // namespace fa

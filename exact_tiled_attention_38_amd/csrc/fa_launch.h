@@ -34,6 +34,14 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 // Query rows per workgroup of the bf16 forward (sets the grid-size limit).
 constexpr int kFwdRowsPerBlock = 256;
 
+// Block-sparse forward: query blocks of kSparseBlockM rows, key blocks of
+// kSparseBlockN keys (the forward's own tiles), selection in CSR form.
+constexpr int kSparseBlockM = 256;
+constexpr int kSparseBlockN = 64;
+hipError_t launch_fwd_bf16_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int* row_ptr, const int* cols, int nnz, const Problem& p,
+                                        hipStream_t stream);
+
 // Decode: Nq queries per head at the end of a sequence of Nk keys.
 struct DecodeProblem {
   int B, H, Hkv, Nq, Nk, d;

@@ -61,6 +61,57 @@ DECODE_WORKLOADS = {
 }
 
 
+# Block-sparse selection on the causal headline shape (B8 H32 N16384 d128):
+# each 256-row query block keeps the first key block (64 keys), the four key
+# blocks under its own rows, and every other key block before it with
+# probability 1/8, drawn per (b, h, query block) from a fixed seed.
+SPARSE_WORKLOADS = {
+    "sparse": dict(name="fwd_block_sparse_causal_bf16_b8h32n16384d128_p8", B=8, H=32, Hkv=32, N=16384,
+                   d=128, dtype="bf16", causal=True, q_mult=1.0, seed=3831, keep=0.125),
+}
+
+
+def sparse_selection(B, H, N, seed, keep, block_m=256, block_n=64):
+    """CSR selection (row_ptr, cols) as int32 numpy arrays, rows ordered (b, h, query block).
+
+    Query block r keeps key block 0, the key blocks covering its own rows,
+    and each earlier key block with probability `keep` (seeded)."""
+    rng = np.random.default_rng(seed)
+    n_qb, n_kb = -(-N // block_m), -(-N // block_n)
+    per = block_m // block_n
+    row_ptr, cols = [0], []
+    for _ in range(B * H):
+        for r in range(n_qb):
+            diag = set(range(r * per, min(n_kb, (r + 1) * per)))
+            earlier = np.arange(0, r * per)
+            chosen = set(earlier[rng.random(earlier.shape[0]) < keep].tolist()) | diag | {0}
+            cols.extend(sorted(chosen))
+            row_ptr.append(len(cols))
+    return np.array(row_ptr, dtype=np.int32), np.array(cols, dtype=np.int32)
+
+
+def sparse_visible_pairs(N, row_ptr, cols, n_heads, causal, block_m=256, block_n=64):
+    """Number of (query, key) pairs the selection keeps, over all heads (for FLOP counts)."""
+    n_qb = -(-N // block_m)
+    total = 0
+    r_idx = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    qb = r_idx % n_qb
+    q_lo, q_hi = qb * block_m, np.minimum(N, (qb + 1) * block_m)
+    k_lo, k_hi = cols.astype(np.int64) * block_n, np.minimum(N, (cols.astype(np.int64) + 1) * block_n)
+    if not causal:
+        total = int(np.sum((q_hi - q_lo) * (k_hi - k_lo)))
+    else:
+        # pairs with k <= q inside each block rectangle: per query row i,
+        # clip(min(i + 1, j1) - j0, 0), summed over the rows (in chunks of blocks)
+        off = np.arange(block_m)
+        for c0 in range(0, q_lo.shape[0], 8192):
+            i = q_lo[c0:c0 + 8192, None] + off[None, :]
+            valid = i < q_hi[c0:c0 + 8192, None]
+            cnt = np.clip(np.minimum(i + 1, k_hi[c0:c0 + 8192, None]) - k_lo[c0:c0 + 8192, None], 0, None)
+            total += int((cnt * valid).sum())
+    return total
+
+
 def make_decode_inputs(cfg, device):
     """Seeded bf16 q [B, H, Nq, d] and k, v [B, Hkv, Nk, d], i.i.d. N(0, 1)."""
     gen = torch.Generator(device=device)

@@ -108,6 +108,33 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * Block-sparse forward: attention restricted to selected blocks ("Attention
+ * and KV Compression", "The composability point": with sparse selection the
+ * tiled kernel runs on the selected blocks only). The (query, key) plane of
+ * each head is cut into blocks of FA_SPARSE_BLOCK_M query rows by
+ * FA_SPARSE_BLOCK_N keys (the forward's own tiles); query block r of head
+ * (b, h), r' = (b * H + h) * ceil(N / FA_SPARSE_BLOCK_M) + r, attends to the
+ * key blocks cols[row_ptr[r'] .. row_ptr[r' + 1]). Pairs outside the listed
+ * blocks are excluded from the softmax, and with causal = 1 so are keys after
+ * the query inside listed blocks. Unselected blocks are never loaded.
+ *   q, o         : bf16 [B, H, N, d];  k, v : const bf16 [B, Hkv, N, d]
+ *   lse          : fp32 [B, H, N]; a row that sees no key gets O = 0, lse = -inf
+ *   row_ptr      : const int32 [B * H * ceil(N / FA_SPARSE_BLOCK_M) + 1], device memory
+ *   cols         : const int32 [nnz], device memory; key block indices
+ *                  (0 .. ceil(N / FA_SPARSE_BLOCK_N) - 1), any order, no
+ *                  repeats within a row (a repeat would count its keys twice)
+ * The list is read on the device only: offsets are clamped to [0, nnz] and
+ * block indices to their range, so malformed lists give wrong results but
+ * never an out-of-bounds access. Heads may be shared as in fa_forward_gqa.
+ * row_ptr and cols must be 4-byte aligned; other rules as fa_forward.
+ */
+#define FA_SPARSE_BLOCK_M 256
+#define FA_SPARSE_BLOCK_N 64
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* row_ptr, const int* cols, int nnz, int B, int H, int Hkv, int N,
+                            int d, int causal, float scale, hipStream_t stream);
+
+/*
  * Forward, fp32 inputs, fp32 arithmetic, fp32 output; same tiling and online
  * softmax as fa_forward, without bf16 rounding anywhere (for checks that need
  * fp32 accuracy). Same arguments, all tensors fp32.

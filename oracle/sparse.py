@@ -45,8 +45,20 @@ def forward_block_sparse(q, k, v, scale, causal, row_ptr, cols, block_m, block_n
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n = q.shape[0]
-    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    keep = block_mask(n, row_ptr, cols, block_m, block_n, causal)[rows]
+    if rows is None:
+        rows = np.arange(n)
+        keep = block_mask(n, row_ptr, cols, block_m, block_n, causal)
+    else:
+        # the same visibility, built for the requested rows only
+        rows = np.asarray(rows, dtype=np.int64)
+        keep = np.zeros((rows.shape[0], n), dtype=bool)
+        key = np.arange(n)
+        for a, i in enumerate(rows):
+            r = i // block_m
+            listed = np.zeros(n, dtype=bool)
+            for c in cols[row_ptr[r]:row_ptr[r + 1]]:
+                listed[c * block_n:(c + 1) * block_n] = True
+            keep[a] = listed & ((key <= i) if causal else True)
     s = scale * (q[rows] @ k.T)
     s[~keep] = -np.inf
     p, lse = softmax_rows(s)

@@ -107,3 +107,18 @@ def test_planted_transposition_is_caught(monkeypatch):
     monkeypatch.setattr(sparse_mod, "block_mask", lambda nn, rp, cc, m_, n_, c: real(nn, rp, cc, m_, n_, c).T)
     bad, _ = sparse_mod.forward_block_sparse(q, k, v, 0.3, False, row_ptr, cols, bm, bn)
     assert not np.allclose(np.nan_to_num(bad), good, atol=1e-6)
+
+
+def test_row_subset_matches_full():
+    rng = np.random.default_rng(6)
+    n, d, bm, bn = 70, 8, 16, 8
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    lists = _random_selection(rng, -(-n // bm), -(-n // bn), 0.4)
+    lists[0] = sorted(set(lists[0]) | {0})
+    row_ptr, cols = _csr(lists)
+    for causal in (False, True):
+        o, lse = oracle.forward_block_sparse(q, k, v, 0.3, causal, row_ptr, cols, bm, bn)
+        rows = np.array([0, 5, 16, 33, 69])
+        o2, lse2 = oracle.forward_block_sparse(q, k, v, 0.3, causal, row_ptr, cols, bm, bn, rows=rows)
+        np.testing.assert_array_equal(o2, o[rows])
+        np.testing.assert_array_equal(lse2, lse[rows])

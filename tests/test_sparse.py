@@ -1,0 +1,161 @@
+"""GPU parity of the block-sparse forward (fa_forward_block_sparse) against
+the fp64 oracle (oracle/sparse.py).
+
+Blocks are the forward's tiles: 256 query rows by 64 keys. Selections are
+seeded random lists per (b, h, query block), with empty rows, unsorted rows
+and (with the causal mask) blocks wholly above the diagonal. O must meet the
+bf16 rule of tests/parity.py and lse |err| <= 1e-3; rows that see no key
+must give O = 0 and lse = -inf exactly. Selecting every block (non-causal) or
+exactly the causal lower block triangle must reproduce fa_forward bit for
+bit: the same tiles in the same order.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_38_amd import SPARSE_BLOCK_M as BM
+from exact_tiled_attention_38_amd import SPARSE_BLOCK_N as BN
+from exact_tiled_attention_38_amd import forward, forward_block_sparse
+from exact_tiled_attention_38_amd import workloads as W
+from tests.parity import BF16_ATOL, BF16_RTOL, LSE_ATOL, assert_close, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _selection(rng, rows, n_kb, density, shuffle=False, empty_every=0):
+    lists = []
+    for r in range(rows):
+        if empty_every and r % empty_every == empty_every - 1:
+            lists.append([])
+            continue
+        sel = rng.choice(n_kb, size=rng.binomial(n_kb, density), replace=False)
+        sel = rng.permutation(sel) if shuffle else np.sort(sel)
+        lists.append(sel.tolist())
+    row_ptr = np.cumsum([0] + [len(x) for x in lists]).astype(np.int32)
+    cols = np.array([c for x in lists for c in x], dtype=np.int32)
+    return row_ptr, cols
+
+
+def _dev(a):
+    return torch.tensor(a, dtype=torch.int32, device=DEV)
+
+
+def _check(q, k, v, o, lse, causal, scale, row_ptr, cols, rows=None):
+    B, H, N, _ = q.shape
+    g = H // k.shape[1]
+    n_qb = -(-N // BM)
+    for b in range(B):
+        for h in range(H):
+            base = (b * H + h) * n_qb
+            rp = row_ptr[base:base + n_qb + 1] - row_ptr[base]
+            cc = cols[row_ptr[base]:row_ptr[base + n_qb]]
+            o_ref, lse_ref = oracle.forward_block_sparse(host(q[b, h]), host(k[b, h // g]), host(v[b, h // g]),
+                                                         scale, causal, rp, cc, BM, BN, rows=rows)
+            sel = slice(None) if rows is None else rows
+            seen = np.isfinite(lse_ref)
+            og, lg = host(o[b, h])[sel], host(lse[b, h])[sel]
+            assert_close(og[seen], o_ref[seen], BF16_ATOL, BF16_RTOL, f"o head {(b, h)}")
+            assert_close(lg[seen], lse_ref[seen], LSE_ATOL, 0.0, f"lse head {(b, h)}")
+            assert np.all(og[~seen] == 0) and np.all(lg[~seen] == -np.inf), f"unseen rows of head {(b, h)}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,density,shuffle", [(1, 1.0, False), (65, 0.6, False), (300, 0.5, True),
+                                               (700, 0.4, True), (1100, 0.25, False)])
+def test_block_sparse_shapes(N, density, shuffle, d, causal):
+    _say("sparse", N, density, shuffle, d, causal)
+    B, H, Hkv = 2, 4, 2
+    rng = np.random.default_rng(5000 + N + d + causal)
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=5100 + N + d), DEV, shape=(B, H, N, d), kv_heads=Hkv)
+    n_qb, n_kb = -(-N // BM), -(-N // BN)
+    row_ptr, cols = _selection(rng, B * H * n_qb, n_kb, density, shuffle, empty_every=5)
+    scale = 1 / math.sqrt(d)
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(cols), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    _check(q, k, v, o, lse, causal, scale, row_ptr, cols)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_selection_is_the_dense_forward_bitwise(causal, d):
+    _say("sparse == dense", causal, d)
+    B, H, N = 2, 2, 777
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=5200 + d), DEV, shape=(B, H, N, d))
+    n_qb, n_kb, per = -(-N // BM), -(-N // BN), BM // BN
+    lists = [list(range(min(n_kb, (r + 1) * per))) if causal else list(range(n_kb))
+             for _ in range(B * H) for r in range(n_qb)]
+    row_ptr = np.cumsum([0] + [len(x) for x in lists]).astype(np.int32)
+    cols = np.array([c for x in lists for c in x], dtype=np.int32)
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(cols), causal=causal)
+    o_d, lse_d = forward(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_d) and torch.equal(lse, lse_d)
+
+
+def test_nothing_selected():
+    _say("sparse empty")
+    B, H, N, d = 1, 2, 500, 128
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=5300), DEV, shape=(B, H, N, d))
+    row_ptr = np.zeros(B * H * -(-N // BM) + 1, dtype=np.int32)
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(np.zeros(0, dtype=np.int32)))
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+def test_malformed_lists_stay_in_bounds():
+    """Offsets past nnz or decreasing, block indices out of range: clamped on
+    the device (never an out-of-bounds read); the result equals the oracle on
+    the clamped selection."""
+    _say("sparse malformed")
+    B, H, N, d = 1, 1, 600, 64
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=5400), DEV, shape=(B, H, N, d))
+    n_kb = -(-N // BN)
+    cols = np.array([-7, 3, 10**6, 5, 2], dtype=np.int32)        # clamp to 0, 3, n_kb-1, 5, 2
+    row_ptr = np.array([0, 3, 2, 99], dtype=np.int32)             # rows: [0,3), empty, [2,5)
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(cols))
+    torch.cuda.synchronize()
+    clamped_cols = np.clip(cols, 0, n_kb - 1)
+    rp = np.array([0, 3, 3, 6], dtype=np.int64)
+    cc = np.concatenate([clamped_cols[0:3], clamped_cols[2:5]])
+    _check(q, k, v, o, lse, False, 1 / math.sqrt(d), rp.astype(np.int32), cc)
+
+
+def test_binding_checks():
+    q = torch.zeros(1, 2, 300, 64, dtype=torch.bfloat16, device=DEV)
+    good = torch.zeros(3, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="row_ptr must have"):
+        forward_block_sparse(q, q, q, torch.zeros(4, dtype=torch.int32, device=DEV), good)
+    with pytest.raises(TypeError, match="int32"):
+        forward_block_sparse(q, q, q, torch.zeros(5, dtype=torch.int64, device=DEV), good)
+
+
+def test_bench_workload_sampled_rows():
+    """The benchmark's selection on B8 H32 N16384 d128 causal: sampled rows of
+    sampled heads against the oracle."""
+    cfg = W.SPARSE_WORKLOADS["sparse"]
+    _say("sparse workload", cfg["name"])
+    q, k, v = W.make_inputs(cfg, DEV)
+    row_ptr, cols = W.sparse_selection(cfg["B"], cfg["H"], cfg["N"], cfg["seed"], cfg["keep"])
+    scale = 1 / math.sqrt(cfg["d"])
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(cols), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    N, n_qb = cfg["N"], -(-cfg["N"] // BM)
+    rows = W.sample_rows(N, 64, cfg["seed"] + 1)
+    for b, h in W.sample_heads(cfg["B"], cfg["H"], 3, cfg["seed"] + 2):
+        base = (b * cfg["H"] + h) * n_qb
+        rp = row_ptr[base:base + n_qb + 1] - row_ptr[base]
+        cc = cols[row_ptr[base]:row_ptr[base + n_qb]]
+        o_ref, lse_ref = oracle.forward_block_sparse(host(q[b, h]), host(k[b, h]), host(v[b, h]), scale, True,
+                                                     rp, cc, BM, BN, rows=rows)
+        assert_close(host(o[b, h])[rows], o_ref, BF16_ATOL, BF16_RTOL, f"o head {(b, h)}")
+        assert_close(host(lse[b, h])[rows], lse_ref, LSE_ATOL, 0.0, f"lse head {(b, h)}")
