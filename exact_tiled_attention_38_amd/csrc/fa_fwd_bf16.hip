@@ -125,7 +125,8 @@ template <int D, int NW, int BN, int S, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(64 * NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int N, int n_qtiles, int group, float c2, BlockList sel) {
+                float* __restrict__ LSE, int N, int n_qtiles, int group, float c2,
+                const int* __restrict__ sel_row_ptr, const int* __restrict__ sel_cols, int sel_nnz) {
   using C = FwdCfg<D, NW, BN, S>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -161,23 +162,23 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int n_tiles, sel_base = 0;
   if constexpr (SPARSE) {
     const int r = bh * n_qtiles + t;
-    const int beg = min(max(sel.row_ptr[r], 0), sel.nnz);
-    const int end = min(max(sel.row_ptr[r + 1], beg), sel.nnz);
+    // (read-only, uniform: scalar loads, which do not wait on the tile loads)
+    const int beg = min(max(sel_row_ptr[r], 0), sel_nnz);
+    const int end = min(max(sel_row_ptr[r + 1], beg), sel_nnz);
     sel_base = __builtin_amdgcn_readfirstlane(beg);
     n_tiles = __builtin_amdgcn_readfirstlane(end - beg);
   } else {
     const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
     n_tiles = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);
   }
-  // first key of tile t (tiles past the last repeat the last one)
+  // first key of tile t (tiles past the last repeat the last one); for the
+  // block-sparse list in two parts, the read (list_entry) and the clamp
+  // into range (entry_key), so a read can be issued well before its use
+  auto list_entry = [&](int t) { return sel_cols[sel_base + min(t, n_tiles - 1)]; };
+  auto entry_key = [&](int e) { return min(max(e, 0), (N - 1) / BN) * BN; };
   auto tile_key = [&](int t) {
-    const int tt = min(t, n_tiles - 1);
-    if constexpr (SPARSE) {
-      const int kb = min(max(sel.cols[sel_base + tt], 0), (N - 1) / BN);
-      return __builtin_amdgcn_readfirstlane(kb * BN);
-    } else {
-      return tt * BN;
-    }
+    if constexpr (SPARSE) return entry_key(list_entry(t));
+    else return min(t, n_tiles - 1) * BN;
   };
   if constexpr (SPARSE) {
     if (n_tiles == 0) {  // nothing selected: no key is visible to these rows
@@ -212,9 +213,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Tile t goes to ring slot t % S. Past the last tile the loads repeat the
   // last tile into the (unused) slot, so every step issues the same number
   // of loads and the wait count below is a constant.
-  auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA]) {
+  auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA], int k0) {
     const int slot = slot0 + (t & (S - 1));
-    const int k0 = tile_key(t);
     const char* base = (const char*)(src + (size_t)k0 * D);
     FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024;
     if (k0 + BN <= N) {
@@ -226,8 +226,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int i = 0; i < C::NDMA; ++i) dma16(base, clamp_row(off[i], lim), dst + i * 1024);
     }
   };
-  auto load_k = [&](int t) { load_tile(Kh, t, 0, dk_off); };
-  auto load_v = [&](int t) { load_tile(Vh, t, S, dv_off); };
+  auto load_k = [&](int t, int k0) { load_tile(Kh, t, 0, dk_off, k0); };
+  auto load_v = [&](int t, int k0) { load_tile(Vh, t, S, dv_off, k0); };
 
   // ---- Q^T operand: lane holds Q[qrow][16c + 8h .. +7]
   bf16x8_t qf[D / 16];
@@ -432,12 +432,23 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // the tiles to all waves.
 #pragma unroll
   for (int t = 0; t + 2 < S; ++t) {
-    load_k(t);
-    load_v(t);
+    const int k0 = tile_key(t);
+    load_k(t, k0);
+    load_v(t, k0);
   }
-  load_k(S - 2);
-  load_k(S - 1);
+  load_k(S - 2, tile_key(S - 2));
+  load_k(S - 1, tile_key(S - 1));
   wait_loads_and_barrier<C::INFLIGHT>();
+  // Block-sparse: the first keys of the tiles a step loads (u+S-2 for V, u+S
+  // for K) and masks (u) come from the list; they are read one step ahead
+  // (scalar loads) and passed along, so no step waits for its own list reads.
+  int kw0 = 0, kw1 = 0, kw2 = 0, km = 0;  // raw list entries of tiles u+S-2, u+S-1, u+S and u
+  if constexpr (SPARSE) {
+    kw0 = list_entry(S - 2);
+    kw1 = list_entry(S - 1);
+    kw2 = list_entry(S);
+    km = list_entry(0);
+  }
 
   f32x16_t sA[BN / 32], sB[BN / 32];
   bf16x8_t pA[BN / 16], pB[BN / 16];
@@ -458,13 +469,20 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // kept live across the loop), row max and alpha.
   auto step_head = [&](int u, f32x16_t (&s_cur)[BN / 32], int& kb0, int& vb0, int v_tile,
                   float& m_use, float& alpha) {
-    load_v(u + S - 2);
-    load_k(u + S);
     if constexpr (SPARSE) {
+      const int nk = list_entry(u + S + 1), nm = list_entry(u + 1);  // for the next step
+      load_v(u + S - 2, entry_key(kw0));
+      load_k(u + S, entry_key(kw2));
       // the even-count padding step (u = n_tiles) is masked entirely
-      const int k0 = u < n_tiles ? tile_key(u) : N;
+      const int k0 = u < n_tiles ? entry_key(km) : N;
       if (k0 >= N || (CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
+      kw0 = kw1;
+      kw1 = kw2;
+      kw2 = nk;
+      km = nm;
     } else {
+      load_v(u + S - 2, tile_key(u + S - 2));
+      load_k(u + S, tile_key(u + S));
       const int k0 = u * BN;
       if ((CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
     }
@@ -556,7 +574,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const float c2 = p.scale * kLog2e;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, S, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(C::NT), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     p.N, n_qtiles, p.group(), c2, sel);
+                     p.N, n_qtiles, p.group(), c2, sel.row_ptr, sel.cols, sel.nnz);
   return hipGetLastError();
 }
 
