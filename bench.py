@@ -59,7 +59,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic_causal_b8h32n16384d128.md")
-FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h", "fa_launch.h"]
+FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h"]
 COPY_BYTES = 1 << 30
 
 
@@ -125,6 +125,9 @@ def pmc_summary(fetch_csv, write_csv):
         "#   python bench.py --pmc-summary <out>/fetch/run_counter_collection.csv <out>/write/run_counter_collection.csv",
         "# Counters are KiB per dispatch; each is scaled by the reading of a plain 1 GiB device copy",
         "# (1 GiB read + 1 GiB written) in the same run.",
+        "# Caveat: K and V reach the forward by direct-to-LDS loads, and for the decode kernel, which reads",
+        "# every K/V byte exactly once by the same loads, FETCH_SIZE reads half of those bytes; the fetch",
+        "# figure below is therefore a lower bound on the bytes the forward pulls through the L2.",
         f"kernel_source_sha256: {fwd_source_hash()}",
         f"copy_bytes: {COPY_BYTES}",
         f"copy_fetch_kib: {cf:.1f}",
