@@ -8,6 +8,7 @@ with it. See attention.py (the one-shot definition) and online_softmax.py
 
 from .attention import backward, forward, scores, softmax_rows
 from .decode import forward_decode, forward_decode_heads, merge_partials
+from .fp8 import e4m3_decode, forward_fp8
 from .heads import backward_heads, forward_heads, kv_head
 from .online_softmax import blockwise_forward, online_softmax_row
 from .sparse import block_mask, forward_block_sparse
@@ -27,4 +28,6 @@ __all__ = [
     "merge_partials",
     "block_mask",
     "forward_block_sparse",
+    "e4m3_decode",
+    "forward_fp8",
 ]
