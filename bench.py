@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s fwd (and fwd+bwd) at N=16K d=128 bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU * 4096 FLOP/clk/CU * 2.4 GHz, dense bf16
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 matrix peak, twice the bf16 one
 
 
 def attention_flops(B, H, N, d, causal):
@@ -42,11 +43,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
-    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long", "sparse"],
+    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long", "sparse", "fp8"],
                     help="instead of --config: the same causal 16K shape with 8 (gqa) or 1 (mqa) "
                          "key/value heads shared by the 32 query heads, or a decode workload (one "
                          "query per head against a 16K or 100K-token cache), or the block-sparse "
-                         "forward on the causal 16K shape (first block + diagonal + 1/8 of the rest)")
+                         "forward on the causal 16K shape (first block + diagonal + 1/8 of the rest), "
+                         "or the fp8 (e4m3) forward on the causal 16K shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -327,6 +329,54 @@ def bench_sparse(a, cfg):
     }
 
 
+def bench_fp8(a, cfg):
+    """fp8 (e4m3) forward at the causal headline shape; fp8 MFMA roofline."""
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+    from exact_tiled_attention_38_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    (q, k, v), (qd, kd, vd) = W.make_fp8_inputs(cfg, dev)
+    scale = 1.0 / d ** 0.5
+    step = lambda: fa.forward_fp8(q, k, v, qd, kd, vd, causal=cfg["causal"], scale=scale)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    ms = total_ms / a.steps
+    flops = attention_flops(B, H, N, d, cfg["causal"])
+    launch_avg = sum(per) / len(per)
+    achieved = flops / (launch_avg * 1e-3) / 1e12
+    return {
+        "metric": "attention TFLOP/s fwd at N=16K d=128, fp8 (e4m3) inputs; % of fp8 MFMA peak",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"causal fp8 (e4m3) attention forward, B={B} H={H} N={N} d={d}, bf16 O",
+                   "B": B, "H": H, "N": N, "d": d, "causal": bool(cfg["causal"])},
+        "roofline": {
+            "kernel": "fwd_fp8_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+            "launch_avg_ms": round(launch_avg, 4),
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -344,6 +394,9 @@ def main():
 
     if a.workload and a.workload.startswith("decode"):
         print(json.dumps(bench_decode(a, W.DECODE_WORKLOADS[a.workload])), flush=True)
+        return
+    if a.workload == "fp8":
+        print(json.dumps(bench_fp8(a, W.FP8_WORKLOADS["fp8"])), flush=True)
         return
     if a.workload == "sparse":
         print(json.dumps(bench_sparse(a, W.SPARSE_WORKLOADS["sparse"])), flush=True)

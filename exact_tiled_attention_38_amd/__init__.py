@@ -7,7 +7,8 @@ passes device pointers and the current stream to the library.
 """
 
 from .api import (SPARSE_BLOCK_M, SPARSE_BLOCK_N, backward, backward_workspace_bytes, decode,
-                  decode_workspace_bytes, forward, forward_block_sparse, forward_f32, merge, status_string)
+                  decode_workspace_bytes, forward, forward_block_sparse, forward_f32, forward_fp8, merge,
+                  status_string)
 
-__all__ = ["forward", "forward_f32", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
+__all__ = ["forward", "forward_f32", "forward_fp8", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
            "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]

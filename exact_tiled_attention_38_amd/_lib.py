@@ -23,6 +23,7 @@ SIGNATURES = {
     "fa_forward_gqa": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _p]),
     "fa_forward_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "fa_forward_block_sparse": (_i, [_p] * 7 + [_i] * 7 + [_f, _p]),
+    "fa_forward_fp8": (_i, [_p] * 5 + [_f] * 3 + [_i] * 6 + [_f, _p]),
     "fa_backward_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_backward": (_i, [_p] * 10 + [_i, _i, _i, _i, _i, _f, _p]),
     "fa_backward_gqa": (_i, [_p] * 10 + [_i, _i, _i, _i, _i, _i, _f, _p]),

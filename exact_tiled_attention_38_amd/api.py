@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["forward", "forward_f32", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
+__all__ = ["forward", "forward_f32", "forward_fp8", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
            "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]
 
 # Block sizes of the block-sparse selection (FA_SPARSE_BLOCK_M / _N in include/fa.h).
@@ -234,4 +234,30 @@ def forward_block_sparse(q, k, v, row_ptr, cols, causal=False, scale=None):
         cols_arg.data_ptr(), nnz, B, H, Hkv, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
     )
     _lib.check(rc, "fa_forward_block_sparse")
+    return o, l
+
+
+def forward_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None):
+    """Exact attention of fp8 (e4m3) inputs with per-tensor dequantisation factors. Returns (o, lse).
+
+    q: torch.float8_e4m3fn [B, H, N, 128]; k, v: [B, Hkv, N, 128]. The values
+    attended are code * descale. o is bf16 [B, H, N, 128], lse fp32 [B, H, N].
+    """
+    B, H, N, d = _check([q], ["q"], torch.float8_e4m3fn)
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, Hkv, N, d], got shape {tuple(k.shape)}")
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"k/v have {Hkv} heads, which must divide q's {H} heads")
+    _check([k, v], ["k", "v"], torch.float8_e4m3fn, (B, Hkv, N, d))
+    if k.device != q.device:
+        raise ValueError(f"k is on {k.device}, expected {q.device}")
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = _lib.lib().fa_forward_fp8(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+        float(q_descale), float(k_descale), float(v_descale),
+        B, H, Hkv, N, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_forward_fp8")
     return o, l

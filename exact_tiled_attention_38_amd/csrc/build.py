@@ -22,12 +22,13 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip",
+           "fa_fwd_fp8.hip"]
 # The bf16 forward's row max runs on v_max_f32 without the IEEE-mode NaN
 # quieting that fmaxf otherwise needs (an extra canonicalising op per score):
 # the kernels never see NaN scores from finite inputs.
 _NO_IEEE = ["-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee"]
-PER_FILE_FLAGS = {"fa_fwd_bf16.hip": _NO_IEEE}
+PER_FILE_FLAGS = {"fa_fwd_bf16.hip": _NO_IEEE, "fa_fwd_fp8.hip": _NO_IEEE}
 ARCH = "gfx950"
 
 

@@ -110,6 +110,22 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
   return launch_status(fa::launch_fwd_bf16_block_sparse(q, k, v, o, lse, row_ptr, cols, nnz, p, stream));
 }
 
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, float q_descale,
+                   float k_descale, float v_descale, int B, int H, int Hkv, int N, int d, int causal, float scale,
+                   hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int s = check_common(B, H, N, d, causal, scale);
+  if (s == FA_OK) s = check_kv_heads(H, Hkv);
+  if (s == FA_OK && d != 128) s = FA_ERR_UNSUPPORTED;
+  if (s != FA_OK) return s;
+  for (float f : {q_descale, k_descale, v_descale})
+    if (!(f > 0.f) || !std::isfinite(f)) return FA_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const fa::Problem p{B, H, N, d, causal, scale, Hkv};
+  return launch_status(fa::launch_fwd_fp8(q, k, v, o, lse, p, fa::Fp8Scales{q_descale, k_descale, v_descale}, stream));
+}
+
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int N, int d, int causal, float scale, hipStream_t stream) {
   return fa_forward_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);

@@ -34,6 +34,13 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 // Query rows per workgroup of the bf16 forward (sets the grid-size limit).
 constexpr int kFwdRowsPerBlock = 256;
 
+// fp8 (e4m3) forward: per-tensor dequantisation factors of Q, K and V.
+struct Fp8Scales {
+  float q, k, v;
+};
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const Problem& p,
+                          const Fp8Scales& sc, hipStream_t stream);
+
 // Block-sparse forward: query blocks of kSparseBlockM rows, key blocks of
 // kSparseBlockN keys (the forward's own tiles), selection in CSR form.
 constexpr int kSparseBlockM = 256;

@@ -112,6 +112,38 @@ def sparse_visible_pairs(N, row_ptr, cols, n_heads, causal, block_m=256, block_n
     return total
 
 
+# fp8 (e4m3) forward on the causal headline shape: N(0, 1) values quantised
+# per tensor with the factor amax / 448 (the largest e4m3 value).
+FP8_WORKLOADS = {
+    "fp8": dict(name="fwd_fp8_causal_b8h32n16384d128", B=8, H=32, Hkv=32, N=16384, d=128, causal=True,
+                seed=3841),
+}
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x):
+    """Per-tensor e4m3 codes of x and the dequantisation factor (x ~ codes * factor)."""
+    factor = float(x.abs().max()) / E4M3_MAX
+    factor = factor if factor > 0 else 1.0
+    return (x / factor).to(torch.float8_e4m3fn), factor
+
+
+def make_fp8_inputs(cfg, device, shape=None, kv_heads=None, seed=None):
+    """Seeded e4m3 (q, k, v) and their factors (qd, kd, vd): N(0, 1) drawn in fp32, quantised per tensor."""
+    B, H, N, d = shape or (cfg["B"], cfg["H"], cfg["N"], cfg["d"])
+    Hkv = kv_heads or cfg.get("Hkv") or H
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg["seed"] if seed is None else seed)
+    out, factors = [], []
+    for heads in (H, Hkv, Hkv):
+        x = _randn((B, heads, N, d), gen, device)
+        codes, f = quantize_e4m3(x)
+        out.append(codes.contiguous())
+        factors.append(f)
+        del x
+    return tuple(out), tuple(factors)
+
+
 def make_decode_inputs(cfg, device):
     """Seeded bf16 q [B, H, Nq, d] and k, v [B, Hkv, Nk, d], i.i.d. N(0, 1)."""
     gen = torch.Generator(device=device)

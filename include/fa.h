@@ -135,6 +135,23 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
                             int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * Forward on fp8 inputs: the narrower number format that "Attention and KV
+ * Compression", "What it does and does not change", names as a later
+ * refinement. Q, K, V hold OCP e4m3 codes (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; largest finite 448) with one fp32 dequantisation factor
+ * per tensor: the attention computed is the exact one of code * factor. Both
+ * products run on the fp8 matrix cores with fp32 accumulation; P is rounded
+ * to e4m3 before the PV product (the only rounding beyond fp32), O is bf16.
+ *   q    : const e4m3 [B, H, N, d];  k, v : const e4m3 [B, Hkv, N, d]
+ *   o    : bf16 [B, H, N, d];  lse : fp32 [B, H, N] (of the dequantised scores)
+ *   q_descale, k_descale, v_descale : finite and > 0, else FA_ERR_SCALE
+ * d must be 128 (else FA_ERR_UNSUPPORTED); other rules as fa_forward_gqa.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   float q_descale, float k_descale, float v_descale, int B, int H, int Hkv, int N,
+                   int d, int causal, float scale, hipStream_t stream);
+
+/*
  * Forward, fp32 inputs, fp32 arithmetic, fp32 output; same tiling and online
  * softmax as fa_forward, without bf16 rounding anywhere (for checks that need
  * fp32 accuracy). Same arguments, all tensors fp32.

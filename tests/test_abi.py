@@ -278,3 +278,22 @@ def test_block_sparse_rejects_invalid_arguments(L, kw, code):
     rc = L.fa_forward_block_sparse(*args, kw.get("nnz", 4), 1, 4, kw.get("Hkv", 4), kw.get("N", 300),
                                    kw.get("d", 64), 0, ctypes.c_float(kw.get("scale", 0.125)), None)
     assert rc == CODES[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ptrs=[0, A, A, A, A]), "FA_ERR_NULL"),
+    (dict(d=64), "FA_ERR_UNSUPPORTED"),
+    (dict(Hkv=3), "FA_ERR_SHAPE"),
+    (dict(qd=0.0), "FA_ERR_SCALE"),
+    (dict(kd=float("inf")), "FA_ERR_SCALE"),
+    (dict(vd=float("nan")), "FA_ERR_SCALE"),
+    (dict(scale=-1.0), "FA_ERR_SCALE"),
+    (dict(ptrs=[A, A, A + 4, A, A]), "FA_ERR_ALIGN"),
+])
+def test_fp8_rejects_invalid_arguments(L, kw, code):
+    ptrs = kw.get("ptrs", [A] * 5)
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    f = lambda x: ctypes.c_float(x)
+    rc = L.fa_forward_fp8(*args, f(kw.get("qd", 1.0)), f(kw.get("kd", 1.0)), f(kw.get("vd", 1.0)), 1, 4,
+                          kw.get("Hkv", 4), 256, kw.get("d", 128), 1, f(kw.get("scale", 0.125)), None)
+    assert rc == CODES[code]
