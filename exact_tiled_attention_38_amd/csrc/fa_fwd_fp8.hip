@@ -41,7 +41,7 @@
 #define FA_FP8_BN 64
 #endif
 #ifndef FA_FP8_STAGES
-#define FA_FP8_STAGES 4
+#define FA_FP8_STAGES 8
 #endif
 #ifndef FA_FP8_PINGPONG
 #define FA_FP8_PINGPONG 1
