@@ -121,8 +121,9 @@ struct BlockList {
   int nnz;
 };
 
+// (8 waves per compute unit: one 8-wave workgroup, or two of 4 waves)
 template <int D, int NW, int BN, int S, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int N, int n_qtiles, int group, float c2,
@@ -582,11 +583,14 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            const Problem& p, hipStream_t stream) {
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 8
+#endif
   static_assert(FwdCfg<128, 8, FA_FWD_BN, FA_FWD_STAGES>::BM == kFwdRowsPerBlock,
                 "grid-size limit assumes 256-row blocks");
   if (p.d == 128)
-    return p.causal ? launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, true>(q, k, v, o, lse, p, stream)
-                    : launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, false>(q, k, v, o, lse, p, stream);
+    return p.causal ? launch<128, FA_FWD_NW, FA_FWD_BN, FA_FWD_STAGES, true>(q, k, v, o, lse, p, stream)
+                    : launch<128, FA_FWD_NW, FA_FWD_BN, FA_FWD_STAGES, false>(q, k, v, o, lse, p, stream);
   return p.causal ? launch<64, 8, 64, 4, true>(q, k, v, o, lse, p, stream)
                   : launch<64, 8, 64, 4, false>(q, k, v, o, lse, p, stream);
 }
@@ -594,14 +598,14 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_bf16_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                         const int* row_ptr, const int* cols, int nnz, const Problem& p,
                                         hipStream_t stream) {
-  static_assert(FA_FWD_BN == kSparseBlockN && FwdCfg<128, 8, FA_FWD_BN, FA_FWD_STAGES>::BM == kSparseBlockM,
-                "the block-sparse selection is in units of the forward's tiles");
+  // (its own fixed tile shape: the selection is in units of these tiles)
+  static_assert(FwdCfg<128, 8, kSparseBlockN, 4>::BM == kSparseBlockM, "block-sparse block shape");
   const BlockList sel{row_ptr, cols, nnz};
   if (p.d == 128)
-    return p.causal ? launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, true, true>(q, k, v, o, lse, p, stream, sel)
-                    : launch<128, 8, FA_FWD_BN, FA_FWD_STAGES, false, true>(q, k, v, o, lse, p, stream, sel);
-  return p.causal ? launch<64, 8, 64, 4, true, true>(q, k, v, o, lse, p, stream, sel)
-                  : launch<64, 8, 64, 4, false, true>(q, k, v, o, lse, p, stream, sel);
+    return p.causal ? launch<128, 8, kSparseBlockN, 4, true, true>(q, k, v, o, lse, p, stream, sel)
+                    : launch<128, 8, kSparseBlockN, 4, false, true>(q, k, v, o, lse, p, stream, sel);
+  return p.causal ? launch<64, 8, kSparseBlockN, 4, true, true>(q, k, v, o, lse, p, stream, sel)
+                  : launch<64, 8, kSparseBlockN, 4, false, true>(q, k, v, o, lse, p, stream, sel);
 }
 
 }  // namespace fa
