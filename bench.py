@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for the HBM byte counters)")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
+                    help="no GPU work: turn one rocprofv3 --pmc --kernel-trace run of `bench.py --no-bwd` "
+                         "into the forward's counter record under profiles/ (MFMA busy, LDS bank "
+                         "conflicts, engine clock)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibration-copy --no-bwd` into the traffic record under profiles/")
@@ -61,6 +65,10 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic_causal_b8h32n16384d128.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_counters_causal_b8h32n16384d128.md")
+N_XCD, N_CU, SIMD_PER_CU, FLOP_PER_CLK_CU = 8, 256, 4, 4096
+COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+            "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
 FWD_SOURCES = ["fa_fwd_bf16.hip", "fa_device.h"]
 COPY_BYTES = 1 << 30
 
@@ -75,6 +83,69 @@ def fwd_source_hash():
         with open(os.path.join(ROOT, "exact_tiled_attention_38_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def read_record(path):
+    """key: value lines of a committed record, or {} when there is none or the
+    forward's sources changed since it was taken."""
+    try:
+        rec = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+        return rec if rec.get("kernel_source_sha256") == fwd_source_hash() else {}
+    except OSError:
+        return {}
+
+
+def counters_summary(counter_csv, trace_csv):
+    """Write the forward's counter record from one --pmc --kernel-trace run.
+
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the engine clock during the
+    kernel is GRBM_GUI_ACTIVE / 8 / duration; MFMA busy is
+    SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); the LDS bank-conflict
+    rate is SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    import csv
+
+    vals = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if "fwd_bf16_kernel" in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    durs = []
+    for r in csv.DictReader(open(trace_csv)):
+        if "fwd_bf16_kernel" in r["Kernel_Name"]:
+            durs.append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+    mean = lambda k: sum(vals[k]) / len(vals[k])
+    dur = sum(durs) / len(durs)
+    cycles = mean("GRBM_GUI_ACTIVE") / N_XCD
+    sclk = cycles / dur / 1e9
+    mfma = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * N_CU * SIMD_PER_CU)
+    conf = mean("SQ_LDS_BANK_CONFLICT") / max(mean("SQ_LDS_IDX_ACTIVE"), 1.0)
+    adj_peak = N_CU * FLOP_PER_CLK_CU * sclk * 1e9 / 1e12
+    lines = [
+        "# Counters of fwd_bf16_kernel, causal bf16 attention forward B=8 H=32 N=16384 d=128, one MI355X",
+        "# Command (from the repository root, cd /tmp && export TMPDIR=/tmp first):",
+        "#   rocprofv3 --pmc " + " ".join(COUNTERS) + " --kernel-trace --output-format csv -d <out>/ctr -o run \\",
+        "#       -- python3 <repo>/bench.py --steps 2 --warmup 0 --no-bwd --no-cpu-baseline",
+        "#   python bench.py --counters-summary <out>/ctr/run_counter_collection.csv <out>/ctr/run_kernel_trace.csv",
+        "# GRBM_GUI_ACTIVE is summed over the 8 XCDs: engine clock = GRBM_GUI_ACTIVE / 8 / kernel duration.",
+        "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x 256 CU x 4 SIMD).",
+        "# (the profiled launches run somewhat slower than unprofiled ones; the fractions are what they measure)",
+        f"kernel_source_sha256: {fwd_source_hash()}",
+        f"launches: {len(durs)}",
+        f"duration_ms: {dur * 1e3:.3f}",
+        f"engine_clock_ghz: {sclk:.3f}",
+        f"clock_adjusted_peak_tflops: {adj_peak:.1f}",
+        f"mfma_busy_frac: {mfma:.4f}",
+        f"lds_bank_conflict_frac: {conf:.4f}",
+        f"mfma_instructions: {mean('SQ_INSTS_MFMA'):.4g}",
+        f"valu_instructions: {mean('SQ_INSTS_VALU'):.4g}",
+        f"lds_instructions: {mean('SQ_INSTS_LDS'):.4g}",
+    ]
+    with open(COUNTERS_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def read_traffic():
@@ -382,6 +453,9 @@ def main():
     if a.pmc_summary:
         pmc_summary(*a.pmc_summary)
         return
+    if a.counters_summary:
+        counters_summary(*a.counters_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -463,8 +537,24 @@ def main():
     if Hkv != H:
         result["config"]["Hkv"] = Hkv
 
+    result["config"]["cu_count"] = torch.cuda.get_device_properties(dev).multi_processor_count
     if a.config == 3 and not a.workload:
         result["roofline"]["traffic"] = read_traffic()
+        if result["roofline"]["traffic"]:
+            result["roofline"]["achieved_hbm_gbs"] = round(
+                result["roofline"]["traffic"] / (launch_avg * 1e-3) / 1e9, 1)
+        rec = read_record(COUNTERS_FILE)
+        if rec:
+            # counters of the same kernel (profiled launches), from the committed record
+            result["counters"] = {
+                "mfma_busy_frac": float(rec["mfma_busy_frac"]),
+                "lds_bank_conflict_frac": float(rec["lds_bank_conflict_frac"]),
+                "engine_clock_ghz": float(rec["engine_clock_ghz"]),
+                "clock_adjusted_peak_tflops": float(rec["clock_adjusted_peak_tflops"]),
+                "frac_of_clock_adjusted_peak": round(
+                    result["roofline"]["achieved"] / float(rec["clock_adjusted_peak_tflops"]), 4),
+                "source": os.path.relpath(COUNTERS_FILE, ROOT),
+            }
 
     if not a.no_bwd and "fwd+bwd" in cfg["passes"]:
         ws = torch.empty(fa.backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
