@@ -140,6 +140,9 @@ def counters_summary(counter_csv, trace_csv):
         f"mfma_busy_frac: {mfma:.4f}",
         f"lds_bank_conflict_frac: {conf:.4f}",
         f"mfma_instructions: {mean('SQ_INSTS_MFMA'):.4g}",
+        "# each v_mfma_f32_32x32x16_bf16 is 32 x 32 x 16 x 2 = 32768 FLOPs; against the algorithmic count the",
+        "# ratio is 1 + the work of masked diagonal/tail tiles and of the even-count padding step",
+        f"mfma_flops_over_algorithmic: {mean('SQ_INSTS_MFMA') * 32768 / attention_flops(8, 32, 16384, 128, True):.4f}",
         f"valu_instructions: {mean('SQ_INSTS_VALU'):.4g}",
         f"lds_instructions: {mean('SQ_INSTS_LDS'):.4g}",
     ]
@@ -275,10 +278,21 @@ def cpu_baseline(cfg, q, k, v, target_s):
         done += 1
         if elapsed >= target_s:
             break
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rate = flops / elapsed
     return {
-        "value": flops / elapsed / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": int(cores),
+        "cpu_model": cpu_model,
+        "extrapolated_full_workload_seconds": round(attention_flops(B, H, N, d, causal) / rate, 1),
         "kind": "oracle",
         "sample": f"fp64 one-shot oracle on {len(rows)} seeded rows (full score rows) of each of {done} heads "
                   f"of the same workload; rate = algorithmic attention FLOPs of those rows "
@@ -538,6 +552,7 @@ def main():
         result["config"]["Hkv"] = Hkv
 
     result["config"]["cu_count"] = torch.cuda.get_device_properties(dev).multi_processor_count
+    result["config"]["device"] = torch.cuda.get_device_name(dev)
     if a.config == 3 and not a.workload:
         result["roofline"]["traffic"] = read_traffic()
         if result["roofline"]["traffic"]:
@@ -553,6 +568,7 @@ def main():
                 "clock_adjusted_peak_tflops": float(rec["clock_adjusted_peak_tflops"]),
                 "frac_of_clock_adjusted_peak": round(
                     result["roofline"]["achieved"] / float(rec["clock_adjusted_peak_tflops"]), 4),
+                "mfma_flops_over_algorithmic": float(rec["mfma_flops_over_algorithmic"]),
                 "source": os.path.relpath(COUNTERS_FILE, ROOT),
             }
 
