@@ -43,12 +43,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload configuration id (3 = headline)")
-    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long", "sparse", "fp8"],
+    ap.add_argument("--workload", choices=["gqa", "mqa", "decode", "decode_gqa", "decode_long", "sparse", "fp8",
+                                           "gemm_ceiling"],
                     help="instead of --config: the same causal 16K shape with 8 (gqa) or 1 (mqa) "
                          "key/value heads shared by the 32 query heads, or a decode workload (one "
                          "query per head against a 16K or 100K-token cache), or the block-sparse "
                          "forward on the causal 16K shape (first block + diagonal + 1/8 of the rest), "
-                         "or the fp8 (e4m3) forward on the causal 16K shape")
+                         "or the fp8 (e4m3) forward on the causal 16K shape, or (context, not the "
+                         "library) the vendor bf16 GEMM torch.matmul at 16384^3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -58,6 +60,9 @@ def parse():
                     help="no GPU work: turn one rocprofv3 --pmc --kernel-trace run of `bench.py --no-bwd` "
                          "into the forward's counter record under profiles/ (MFMA busy, LDS bank "
                          "conflicts, engine clock)")
+    ap.add_argument("--ceiling-summary", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
+                    help="no GPU work: turn one rocprofv3 --pmc --kernel-trace run of "
+                         "`bench.py --workload gemm_ceiling` into the GEMM ceiling record under profiles/")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibration-copy --no-bwd` into the traffic record under profiles/")
@@ -66,6 +71,9 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic_causal_b8h32n16384d128.md")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_counters_causal_b8h32n16384d128.md")
+CEILING_FILE = os.path.join(ROOT, "profiles", "gemm_bf16_ceiling_m16384n16384k16384.md")
+GEMM_N = 16384
+CEILING_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
 N_XCD, N_CU, SIMD_PER_CU, FLOP_PER_CLK_CU = 8, 256, 4, 4096
 COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
             "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
@@ -149,6 +157,95 @@ def counters_summary(counter_csv, trace_csv):
     with open(COUNTERS_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def time_vendor_gemm(steps, warmup):
+    """The vendor's bf16 GEMM (torch.matmul -> hipBLASLt) at 16384^3 on the same
+    part: what a dense matrix product reaches here under the same power and
+    clock limits. Context for the attention kernels' roofline, not a library
+    path. Returns (ms per product, TFLOP/s)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    x = torch.randn(GEMM_N, GEMM_N, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    y = torch.randn(GEMM_N, GEMM_N, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    z = torch.empty(GEMM_N, GEMM_N, device=dev, dtype=torch.bfloat16)
+    total_ms, _ = time_launches(lambda: torch.matmul(x, y, out=z), steps, warmup, stream)
+    ms = total_ms / steps
+    del x, y, z
+    return ms, 2.0 * GEMM_N ** 3 / (ms * 1e-3) / 1e12
+
+
+def bench_gemm_ceiling(a):
+    import torch
+
+    ms, tflops = time_vendor_gemm(a.steps, a.warmup)
+    dev = torch.device("cuda:0")
+    return {"metric": "vendor bf16 GEMM throughput (context)", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"torch.matmul bf16 {GEMM_N}x{GEMM_N}x{GEMM_N}",
+                       "device": torch.cuda.get_device_name(dev)},
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
+def ceiling_summary(counter_csv, trace_csv):
+    """Write the GEMM ceiling record from one --pmc --kernel-trace run of
+    `bench.py --workload gemm_ceiling`: the GEMM kernel is the one with the
+    most launches of GEMM_N^3 work (the longest total time in the trace)."""
+    import csv
+
+    durs = {}
+    for r in csv.DictReader(open(trace_csv)):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+    name = max(durs, key=lambda k: sum(durs[k]))
+    vals = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Kernel_Name"] == name:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = lambda k: sum(vals[k]) / len(vals[k])
+    dur = sum(durs[name]) / len(durs[name])
+    cycles = mean("GRBM_GUI_ACTIVE") / N_XCD
+    sclk = cycles / dur / 1e9
+    mfma = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * N_CU * SIMD_PER_CU)
+    tflops = 2.0 * GEMM_N ** 3 / dur / 1e12
+    lines = [
+        f"# Vendor bf16 GEMM (torch.matmul -> hipBLASLt), {GEMM_N}x{GEMM_N}x{GEMM_N}, one MI355X: the ceiling a",
+        "# dense matrix product reaches on this part under its power and clock limits.",
+        "# Command (from the repository root, cd /tmp && export TMPDIR=/tmp first):",
+        "#   rocprofv3 --pmc " + " ".join(CEILING_COUNTERS) + " --kernel-trace --output-format csv -d <out>/gemm -o run \\",
+        "#       -- python3 <repo>/bench.py --workload gemm_ceiling --steps 5 --warmup 2",
+        "#   python bench.py --ceiling-summary <out>/gemm/run_counter_collection.csv <out>/gemm/run_kernel_trace.csv",
+        "# engine clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+        "# (clock cycles x 256 CU x 4 SIMD). Profiled launches, so the duration is the profiler's.",
+        f"kernel: {name[:120]}",
+        f"launches: {len(durs[name])}",
+        f"duration_ms: {dur * 1e3:.3f}",
+        f"tflops: {tflops:.1f}",
+        f"frac_of_peak: {tflops / PEAK_BF16_TFLOPS:.4f}",
+        f"engine_clock_ghz: {sclk:.3f}",
+        f"mfma_busy_frac: {mfma:.4f}",
+    ]
+    with open(CEILING_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_ceiling():
+    try:
+        rec = {}
+        for line in open(CEILING_FILE):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+        return rec if "tflops" in rec else {}
+    except OSError:
+        return {}
 
 
 def read_traffic():
@@ -470,6 +567,9 @@ def main():
     if a.counters_summary:
         counters_summary(*a.counters_summary)
         return
+    if a.ceiling_summary:
+        ceiling_summary(*a.ceiling_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -488,6 +588,9 @@ def main():
         return
     if a.workload == "sparse":
         print(json.dumps(bench_sparse(a, W.SPARSE_WORKLOADS["sparse"])), flush=True)
+        return
+    if a.workload == "gemm_ceiling":
+        print(json.dumps(bench_gemm_ceiling(a)), flush=True)
         return
     cfg = W.gqa_config(a.workload) if a.workload else W.config(a.config)
     B, H, N, d, causal, scale = cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"], cfg["scale"]
@@ -571,6 +674,20 @@ def main():
                 "mfma_flops_over_algorithmic": float(rec["mfma_flops_over_algorithmic"]),
                 "source": os.path.relpath(COUNTERS_FILE, ROOT),
             }
+        # the vendor's dense bf16 GEMM on this part, timed here the same way: what
+        # a matrix product without softmax work reaches under the same limits
+        # (its clock and MFMA busy fraction come from the committed record)
+        g_ms, g_tf = time_vendor_gemm(min(a.steps, 10), 2)
+        result["ceiling"] = {
+            "vendor_bf16_gemm_tflops": round(g_tf, 2),
+            "workload": f"torch.matmul bf16 {GEMM_N}x{GEMM_N}x{GEMM_N}",
+            "frac_of_vendor_gemm": round(result["roofline"]["achieved"] / g_tf, 4),
+        }
+        ceil = read_ceiling()
+        if ceil:
+            result["ceiling"].update({"record_engine_clock_ghz": float(ceil["engine_clock_ghz"]),
+                                      "record_mfma_busy_frac": float(ceil["mfma_busy_frac"]),
+                                      "source": os.path.relpath(CEILING_FILE, ROOT)})
 
     if not a.no_bwd and "fwd+bwd" in cfg["passes"]:
         ws = torch.empty(fa.backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
