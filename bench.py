@@ -107,7 +107,7 @@ def read_record(path):
         return {}
 
 
-def counters_summary(counter_csv, trace_csv):
+def counters_summary(counter_csv, trace_csv, out=None):
     """Write the forward's counter record from one --pmc --kernel-trace run.
 
     GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the engine clock during the
@@ -154,7 +154,7 @@ def counters_summary(counter_csv, trace_csv):
         f"valu_instructions: {mean('SQ_INSTS_VALU'):.4g}",
         f"lds_instructions: {mean('SQ_INSTS_LDS'):.4g}",
     ]
-    with open(COUNTERS_FILE, "w") as fh:
+    with open(out or COUNTERS_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -193,7 +193,7 @@ def bench_gemm_ceiling(a):
             "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
-def ceiling_summary(counter_csv, trace_csv):
+def ceiling_summary(counter_csv, trace_csv, out=None):
     """Write the GEMM ceiling record from one --pmc --kernel-trace run of
     `bench.py --workload gemm_ceiling`: the GEMM kernel is the one with the
     most launches of GEMM_N^3 work (the longest total time in the trace)."""
@@ -231,15 +231,15 @@ def ceiling_summary(counter_csv, trace_csv):
         f"engine_clock_ghz: {sclk:.3f}",
         f"mfma_busy_frac: {mfma:.4f}",
     ]
-    with open(CEILING_FILE, "w") as fh:
+    with open(out or CEILING_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def read_ceiling():
+def read_ceiling(path=None):
     try:
         rec = {}
-        for line in open(CEILING_FILE):
+        for line in open(path or CEILING_FILE):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
@@ -248,12 +248,12 @@ def read_ceiling():
         return {}
 
 
-def read_traffic():
+def read_traffic(path=None):
     """HBM bytes per forward launch from the committed counter record, or None
     when there is none or the kernel sources changed since it was taken."""
     try:
         rec = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path or TRAFFIC_FILE):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
@@ -264,7 +264,7 @@ def read_traffic():
         return None
 
 
-def pmc_summary(fetch_csv, write_csv):
+def pmc_summary(fetch_csv, write_csv, out=None):
     """Write the traffic record from a FETCH_SIZE run and a WRITE_SIZE run.
 
     Both counters are in KiB per dispatch. Each is scaled by what it reads for
@@ -312,7 +312,7 @@ def pmc_summary(fetch_csv, write_csv):
         f"traffic_bytes_per_launch: {traffic:.0f}",
         f"algorithmic_bytes_per_launch: {algorithmic_fwd_bytes(8, 32, 16384, 128):.0f}",
     ]
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(out or TRAFFIC_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
