@@ -19,12 +19,20 @@
 //     the registers that hold dP^T and P^T, and K^T is read from K's
 //     row-major LDS tile with ds_read_b64_tr_b16 (K is therefore read both by
 //     rows and transposed, and its 16-byte chunks are swizzled for both).
+//   * A step is straight-line code in scheduling slices, one or two MFMAs
+//     each: the scores and dP of the tile's second 32-key block run on the
+//     matrix cores while the vector unit computes the first block's P and
+//     dS, and the second block's P and dS overlap the first dQ products.
+//     LDS operands are read two slices ahead; every accumulator sums in the
+//     order of the plain loop nest, so the schedule does not change results.
 //   * No atomics: every query row's gradient is summed by one wave, so dq is
 //     deterministic; the price is recomputing S and dP a second time (the
 //     dK/dV kernel computes them too).
 //   * Causal: a query block's key range ends at its last row; only tiles on
 //     the diagonal or the ragged tail are masked (tail rows are loaded from
 //     key N-1, finite, and masked).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -184,7 +192,29 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   wait_loads_and_barrier<C::INFLIGHT>();
 
-  for (int u = 0; u < n_tiles; ++u) {
+  // ---- one step (key tile u) as an explicit schedule of scheduling slices:
+  //   S^T, dP^T of key block kb (32 keys; 2 MFMAs per d chunk), kb-major,
+  //     with the gradient of block kb-1 on the vector unit;
+  //   dQ^T += K^T dS^T, 16-key group major, with the last block's gradient
+  //     in the first half of its slices (each group's dS is complete before
+  //     its first product).
+  // Each accumulator sums in the same order as a plain loop nest would. The
+  // LDS operands of a slice are read LA slices ahead (row reads of K and V
+  // for S and dP, transposed reads of K for dQ). MASKED: the tile reaches
+  // past this wave's rows (causal) or past N, and P is masked.
+  constexpr int NCH = D / 16;        // d chunks: S/dP slices per key block
+  constexpr int NKB = BN / 32;       // key blocks of 32
+  constexpr int NA = NKB * NCH;      // S/dP slices
+  constexpr int NJ = D / 32;         // dQ^T row blocks
+  constexpr int NQ = (BN / 16) * NJ; // dQ slices
+  constexpr int LA = 2;
+  constexpr int PPS_A = 8 / NCH;     // gradient pairs per S/dP slice (8 pairs per key block)
+  constexpr int PPS_Q = 16 / NQ;     // gradient pairs per slice in the first half of dQ
+  static_assert(8 % NCH == 0 && 16 % NQ == 0, "slicing");
+  const int u_full = __builtin_amdgcn_readfirstlane(
+      CAUSAL ? min((row0 + 1) / BN, N / BN) : N / BN);  // tiles before it need no mask
+  auto step = [&](int u, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     load_tile(Kh, u + S - 1, 0, dk_off);
     load_tile(Vh, u + S - 1, S, dv_off);
     const int slot = u & (S - 1);
@@ -195,61 +225,70 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     int t0 = (int)(uintptr_t)(lds + slot * C::TILEB) + tr_off0;
     int t1 = (int)(uintptr_t)(lds + slot * C::TILEB) + tr_off1;
     asm volatile("" : "+v"(ka), "+v"(va), "+v"(t0), "+v"(t1));
+    const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - u * BN - 4 * h;
 
-    // S^T = K Q^T and dP^T = V dO^T: BN keys x this wave's 32 queries
-    f32x16_t s[BN / 32], dp[BN / 32];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { s[kb][i] = 0.f; dp[kb][i] = 0.f; }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        const bf16x8_t ka8 = *(const FA_LDS bf16x8_t*)((FA_LDS char*)(uintptr_t)(ka ^ (32 * c)) +
-                                                        kb * 32 * C::ROWB);
-        const bf16x8_t va8 = *(const FA_LDS bf16x8_t*)((FA_LDS char*)(uintptr_t)(va ^ (32 * c)) +
-                                                        kb * 32 * C::ROWB);
-        s[kb] = mfma_32x32x16(ka8, qf[c], s[kb]);
-        dp[kb] = mfma_32x32x16(va8, gf[c], dp[kb]);
-      }
-    }
-
-    // P^T = exp(S^T - lse), dS^T = P^T (dP^T - D) -> bf16, masked on the
-    // diagonal / tail tiles (lane holds keys k0 + 32kb + 8(i/4) + 4h + i%4)
-    const int k0 = u * BN;
-    const bool need_mask = (CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N;
-    const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * h;
-    bf16x8_t ds[BN / 16];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p0 = exp2_fast(fmaf(s[kb][i], c2, -lse2));
-        float p1 = exp2_fast(fmaf(s[kb][i + 1], c2, -lse2));
-        if (need_mask) {
-          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p0 = 0.f;
-          if (kb * 32 + 8 * ((i + 1) >> 2) + ((i + 1) & 3) > lim) p1 = 0.f;
-        }
-        const bf16x2_t d2 = to_bf16x2(p0 * (dp[kb][i] - Dl), p1 * (dp[kb][i + 1] - Dl));
-        ds[2 * kb + (i >> 3)][i & 7] = d2[0];
-        ds[2 * kb + (i >> 3)][(i & 7) + 1] = d2[1];
-      }
-
-    // dQ^T += K^T dS^T (keys are the contraction, in the score registers'
-    // order, which the two transposed reads reproduce)
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-#pragma unroll
-      for (int kc = 0; kc < BN / 16; ++kc) {
+    bf16x8_t rk[NA], rv[NA], rt[NQ];
+    auto issue = [&](int x) {
+      if (x < NA) {
+        const int kb = x / NCH, c = x % NCH;
+        rk[x] = *(const FA_LDS bf16x8_t*)((FA_LDS char*)(uintptr_t)(ka ^ (32 * c)) + kb * 32 * C::ROWB);
+        rv[x] = *(const FA_LDS bf16x8_t*)((FA_LDS char*)(uintptr_t)(va ^ (32 * c)) + kb * 32 * C::ROWB);
+      } else if (x < NA + NQ) {
+        const int y = x - NA, kc = y / NJ, j = y % NJ;
         const int rb = ((kc >> 1) * 32 + 16 * (kc & 1)) * C::ROWB;
-        const bf16x4_t lo = lds_read_tr4((FA_LDS char*)(uintptr_t)(t0 ^ (64 * j)) + rb);
-        const bf16x4_t hi = lds_read_tr4((FA_LDS char*)(uintptr_t)(t1 ^ (64 * j)) + rb);
-        acc[j] = mfma_32x32x16(concat8(lo, hi), ds[kc], acc[j]);
+        rt[y] = concat8(lds_read_tr4((FA_LDS char*)(uintptr_t)(t0 ^ (64 * j)) + rb),
+                        lds_read_tr4((FA_LDS char*)(uintptr_t)(t1 ^ (64 * j)) + rb));
       }
+    };
+    // P^T = exp(S^T - lse), dS^T = P^T (dP^T - D) -> bf16 for elements 2pr,
+    // 2pr+1 of key block kb (lane holds keys 32kb + 8(i/4) + 4h + i%4)
+    f32x16_t s[NKB], dp[NKB];
+    bf16x8_t ds[BN / 16];
+    auto grad_pair = [&](int kb, int pr) {
+      const int i = 2 * pr;
+      float p0 = exp2_fast(fmaf(s[kb][i], c2, -lse2));
+      float p1 = exp2_fast(fmaf(s[kb][i + 1], c2, -lse2));
+      if constexpr (MASKED) {
+        if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) p0 = 0.f;
+        if (kb * 32 + 8 * ((i + 1) >> 2) + ((i + 1) & 3) > lim) p1 = 0.f;
+      }
+      const bf16x2_t d2 = to_bf16x2(p0 * (dp[kb][i] - Dl), p1 * (dp[kb][i + 1] - Dl));
+      ds[2 * kb + (i >> 3)][i & 7] = d2[0];
+      ds[2 * kb + (i >> 3)][(i & 7) + 1] = d2[1];
+    };
+
+#pragma unroll
+    for (int x = 0; x < LA; ++x) issue(x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < NA; ++x) {
+      issue(x + LA);
+      const int kb = x / NCH, c = x % NCH;
+      const f32x16_t z = {};
+      s[kb] = mfma_32x32x16(rk[x], qf[c], c == 0 ? z : s[kb]);
+      dp[kb] = mfma_32x32x16(rv[x], gf[c], c == 0 ? z : dp[kb]);
+      if (kb >= 1) {
+#pragma unroll
+        for (int pr = c * PPS_A; pr < (c + 1) * PPS_A; ++pr) grad_pair(kb - 1, pr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int y = 0; y < NQ; ++y) {
+      issue(NA + y + LA);
+      const int kc = y / NJ, j = y % NJ;
+      if (y < NQ / 2) {
+#pragma unroll
+        for (int pr = y * PPS_Q; pr < (y + 1) * PPS_Q; ++pr) grad_pair(NKB - 1, pr);
+      }
+      acc[j] = mfma_32x32x16(rt[y], ds[kc], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_loads_and_barrier<C::INFLIGHT>();
-  }
+  };
+  int u = 0;
+  for (; u < min(u_full, n_tiles); ++u) step(u, std::false_type{});
+  for (; u < n_tiles; ++u) step(u, std::true_type{});
   // no load may still be writing this workgroup's LDS when it exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
