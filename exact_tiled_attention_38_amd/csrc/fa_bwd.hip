@@ -244,17 +244,23 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
     f32x16_t s[2], dp[2];
     bf16x8_t pb[2][2], dsb[2][2];
-    // P and dS (bf16) for elements 2pr, 2pr+1 of block qb; the rows'
-    // lse * log2(e) and D come from the tile's row statistics in LDS
+    // the rows' lse * log2(e) and D for block qb, read from the tile's row
+    // statistics one phase before their use (lane's rows 8g + 4h .. + 3)
+    f32x4_t st_l[2][4], st_d[2][4];
+    auto read_stats = [&](int qb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        st_l[qb][g] = *(const FA_LDS f32x4_t*)&rowstat[slot][0][qb * 32 + 8 * g + 4 * h];
+        st_d[qb][g] = *(const FA_LDS f32x4_t*)&rowstat[slot][1][qb * 32 + 8 * g + 4 * h];
+      }
+    };
+    // P and dS (bf16) for elements 2pr, 2pr+1 of block qb
     auto grad_pair = [&](int qb, int pr) {
       const int i = 2 * pr, g = i >> 2, e = i & 3;
-      const int qi = qb * 32 + 8 * g + 4 * h + e;
-      const f32x2_t l2 = *(const FA_LDS f32x2_t*)&rowstat[slot][0][qi];
-      const f32x2_t d2 = *(const FA_LDS f32x2_t*)&rowstat[slot][1][qi];
-      const float p0 = exp2_fast(fmaf(s[qb][i], c2, -l2[0]));
-      const float p1 = exp2_fast(fmaf(s[qb][i + 1], c2, -l2[1]));
+      const float p0 = exp2_fast(fmaf(s[qb][i], c2, -st_l[qb][g][e]));
+      const float p1 = exp2_fast(fmaf(s[qb][i + 1], c2, -st_l[qb][g][e + 1]));
       const bf16x2_t pp = to_bf16x2(p0, p1);
-      const bf16x2_t dd = to_bf16x2(p0 * (dp[qb][i] - d2[0]), p1 * (dp[qb][i + 1] - d2[1]));
+      const bf16x2_t dd = to_bf16x2(p0 * (dp[qb][i] - st_d[qb][g][e]), p1 * (dp[qb][i + 1] - st_d[qb][g][e + 1]));
       pb[qb][i >> 3][i & 7] = pp[0];
       pb[qb][i >> 3][(i & 7) + 1] = pp[1];
       dsb[qb][i >> 3][i & 7] = dd[0];
@@ -273,6 +279,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     };
 
     bf16x8_t ra[NC], rg[NC];
+    read_stats(0);
     ra[0] = rread(Qs, 0, 0); rg[0] = rread(Gs, 0, 0);
     ra[1] = rread(Qs, 0, 1); rg[1] = rread(Gs, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -289,6 +296,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     if constexpr (need_mask) mask(0);
     // A1 with the softmax gradient of block 0
+    read_stats(1);
     bf16x8_t ta[NB], tg[NB];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
