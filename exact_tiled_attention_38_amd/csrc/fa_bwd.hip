@@ -225,15 +225,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // The tile as an explicit schedule of four phases over its two 32-row
     // query blocks (waves whose keys all follow the tile's queries run it
     // too, fully masked: P = dS = 0, which keeps one straight path):
-    //   A0: S(0), dP(0)                  matrix
-    //   A1: S(1), dP(1)  with P/dS(0)    matrix + vector
-    //   B0: dV, dK(0)    with P/dS(1)    matrix + vector
-    //   B1: dV, dK(1)                    matrix
+    //   A0: S(0), dP(0)                                 matrix
+    //   A1: S(1), dP(1)  with 6 of the 8 pairs of P/dS(0) matrix + vector
+    //   B0: dV, dK(0)    with the rest of P/dS(0), then
+    //                    the first half of P/dS(1)        matrix + vector
+    //   B1: dV, dK(1)    with the second half of P/dS(1)  matrix + vector
+    // (each half of a block's P/dS is complete before the first slice that
+    // multiplies it; spreading it this way keeps any phase from carrying
+    // more vector work than its matrix instructions can cover)
     // Each matrix instruction closes a scheduling slice; its LDS reads are
     // issued two slices ahead. S and dP: lane holds key `key`, queries
     // qb*32 + 8(i/4) + 4h + i%4.
     constexpr int NC = D / 16;       // S/dP slices per query block
     constexpr int NB = 2 * (D / 32); // dV/dK slices per query block (jj, j)
+    // gradient pairs of block 0 moved from A1 into the first slices of B0
+    constexpr int K0 = 2;
+    static_assert(K0 <= NB / 2 && K0 < NB, "block 0 must be complete before B0 uses its second half");
     auto rread = [&](const FA_LDS char* base, int qb, int c) {
       return *(const FA_LDS bf16x8_t*)(base + qb * 32 * C::ROWB + (ro ^ (32 * c)));
     };
@@ -307,12 +314,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       s[1] = mfma_32x32x16(ra[c], kf[c], c == 0 ? z : s[1]);
       dp[1] = mfma_32x32x16(rg[c], vf[c], c == 0 ? z : dp[1]);
 #pragma unroll
-      for (int pr = c * (8 / NC); pr < (c + 1) * (8 / NC); ++pr) grad_pair(0, pr);
+      for (int pr = c * (8 - K0) / NC; pr < (c + 1) * (8 - K0) / NC; ++pr) grad_pair(0, pr);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // (P and dS of block 0 are complete here: keep the compiler from sinking
-    // them past the branch below, away from these matrix instructions)
-    asm volatile("" :: "v"(pb[0][0]), "v"(pb[0][1]), "v"(dsb[0][0]), "v"(dsb[0][1]));
+    // (the first half of block 0's P and dS is complete here: keep the
+    // compiler from sinking it past the branch below, away from these
+    // matrix instructions)
+    asm volatile("" :: "v"(pb[0][0]), "v"(dsb[0][0]));
     if constexpr (need_mask) mask(1);
     // B0 (dV^T += dO^T P, dK^T += Q^T dS over block 0) with block 1's gradient
 #pragma unroll
@@ -321,19 +329,29 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (mn < NB) { ta[mn] = tread(Qs, 0, mn); tg[mn] = tread(Gs, 0, mn); }
       else { ta[mn - NB] = tread(Qs, 1, mn - NB); tg[mn - NB] = tread(Gs, 1, mn - NB); }
       const int jj = m / (D / 32), j = m % (D / 32);
+      // block 0's last K0 pairs first (its second half is used from slice
+      // NB/2 on), then the first half of block 1 (used in B1)
+      if (m < K0) grad_pair(0, 8 - K0 + m);
+      else {
+#pragma unroll
+        for (int pr = (m - K0) * 4 / (NB - K0); pr < (m - K0 + 1) * 4 / (NB - K0); ++pr) grad_pair(1, pr);
+      }
       dvacc[j] = mfma_32x32x16(tg[m], pb[0][jj], dvacc[j]);
       dkacc[j] = mfma_32x32x16(ta[m], dsb[0][jj], dkacc[j]);
-#pragma unroll
-      for (int pr = m * (8 / NB); pr < (m + 1) * (8 / NB); ++pr) grad_pair(1, pr);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("" :: "v"(pb[1][0]), "v"(pb[1][1]), "v"(dsb[1][0]), "v"(dsb[1][1]));
+    asm volatile("" :: "v"(pb[1][0]), "v"(dsb[1][0]));
     // B1
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
       const int mn = m + 2;
       if (mn < NB) { ta[mn] = tread(Qs, 1, mn); tg[mn] = tread(Gs, 1, mn); }
       const int jj = m / (D / 32), j = m % (D / 32);
+      // the second half of block 1, used from slice NB/2 on
+      if (m < NB / 2) {
+#pragma unroll
+        for (int pr = 4 + m * 8 / NB; pr < 4 + (m + 1) * 8 / NB; ++pr) grad_pair(1, pr);
+      }
       dvacc[j] = mfma_32x32x16(tg[m], pb[1][jj], dvacc[j]);
       dkacc[j] = mfma_32x32x16(ta[m], dsb[1][jj], dkacc[j]);
       __builtin_amdgcn_sched_barrier(0);
