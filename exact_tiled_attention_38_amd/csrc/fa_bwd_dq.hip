@@ -196,8 +196,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   //   S^T, dP^T of key block kb (32 keys; 2 MFMAs per d chunk), kb-major,
   //     with the gradient of block kb-1 on the vector unit;
   //   dQ^T += K^T dS^T, 16-key group major, with the last block's gradient
-  //     in the first half of its slices (each group's dS is complete before
-  //     its first product).
+  //     in the first three quarters of its slices (each group's dS is
+  //     complete before its first product).
   // Each accumulator sums in the same order as a plain loop nest would. The
   // LDS operands of a slice are read LA slices ahead (row reads of K and V
   // for S and dP, transposed reads of K for dQ). MASKED: the tile reaches
@@ -209,8 +209,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NQ = (BN / 16) * NJ; // dQ slices
   constexpr int LA = 2;
   constexpr int PPS_A = 8 / NCH;     // gradient pairs per S/dP slice (8 pairs per key block)
-  constexpr int PPS_Q = 16 / NQ;     // gradient pairs per slice in the first half of dQ
-  static_assert(8 % NCH == 0 && 16 % NQ == 0, "slicing");
+  constexpr int NQG = 3 * NJ;        // dQ slices that carry the last block's gradient
+  static_assert(8 % NCH == 0 && NKB == 2, "slicing: two 32-key blocks per tile");
   const int u_full = __builtin_amdgcn_readfirstlane(
       CAUSAL ? min((row0 + 1) / BN, N / BN) : N / BN);  // tiles before it need no mask
   auto step = [&](int u, auto masked) {
@@ -277,9 +277,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int y = 0; y < NQ; ++y) {
       issue(NA + y + LA);
       const int kc = y / NJ, j = y % NJ;
-      if (y < NQ / 2) {
+      // its first half (pairs 0-3) is multiplied from slice 2 NJ on, its
+      // second half from slice 3 NJ: spread over the first 3 NJ slices
+      if (y < NQG) {
 #pragma unroll
-        for (int pr = y * PPS_Q; pr < (y + 1) * PPS_Q; ++pr) grad_pair(NKB - 1, pr);
+        for (int pr = y * 8 / NQG; pr < (y + 1) * 8 / NQG; ++pr) grad_pair(NKB - 1, pr);
       }
       acc[j] = mfma_32x32x16(rt[y], ds[kc], acc[j]);
       __builtin_amdgcn_sched_barrier(0);
