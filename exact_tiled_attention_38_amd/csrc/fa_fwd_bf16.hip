@@ -443,7 +443,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Block-sparse: the first keys of the tiles a step loads (u+S-2 for V, u+S
   // for K) and masks (u) come from the list; they are read one step ahead
   // (scalar loads) and passed along, so no step waits for its own list reads.
-  int kw0 = 0, kw1 = 0, kw2 = 0, km = 0;  // raw list entries of tiles u+S-2, u+S-1, u+S and u
+  // raw list entries of tiles u+S-2, u+S-1, u+S (loads), u (mask) and u-1
+  int kw0 = 0, kw1 = 0, kw2 = 0, km = 0, km_prev = 0;
   if constexpr (SPARSE) {
     kw0 = list_entry(S - 2);
     kw1 = list_entry(S - 1);
@@ -480,6 +481,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       kw0 = kw1;
       kw1 = kw2;
       kw2 = nk;
+      km_prev = km;
       km = nm;
     } else {
       load_v(u + S - 2, tile_key(u + S - 2));
@@ -505,23 +507,39 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     alpha = exp2_fast(m_run - m_use);
     m_run = m_new;
   };
+  // Block-sparse: a tile every key of which follows this wave's last row (or
+  // lies past N, as the padding step's does) has P = 0 exactly, and the wave
+  // skips its PV product (the scores and softmax stay on the straight path,
+  // which keeps the registers where they are). Short lists make such tiles
+  // a noticeable share of the work; the dense instances keep the branch-free
+  // step, which measured faster there.
+  auto dead = [&](int t, int e) {
+    if constexpr (SPARSE) {
+      const int k0 = t < n_tiles ? entry_key(e) : N;
+      return k0 >= N || (CAUSAL && k0 > row0 + 31);
+    } else {
+      return false;
+    }
+  };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p)[BN / 16]) {
     int kb0, vb0;
     float m_use, alpha;
+    const bool live = !dead(u, km);
     step_head(u, s_cur, kb0, vb0, u, m_use, alpha);
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
-    pv(vb0, p);
+    if (live) pv(vb0, p);
     wait_loads_and_barrier<C::INFLIGHT>();
   };
   auto step_hi = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first) {
     int kb0, vb0;
     float m_use, alpha;
+    const bool prev_live = !first && !dead(u - 1, km_prev);
     step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha);
-    if (!first) pv(vb0, p_prev);
+    if (prev_live) pv(vb0, p_prev);
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
@@ -541,7 +559,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       step_hi(u + 1, sA, sB, pA, pB, false);
     }
     step_hi(n_steps - 1, sB, sA, pB, pA, false);
-    pv(v_addr((n_steps - 1) & (S - 1)), pB);
+    // (the list entries have moved on by one step: km_prev is tile n_steps - 1's)
+    if (!dead(n_steps - 1, km_prev)) pv(v_addr((n_steps - 1) & (S - 1)), pB);
   }
   // no load may still be writing this workgroup's LDS when it exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
