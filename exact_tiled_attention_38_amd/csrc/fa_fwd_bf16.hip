@@ -44,13 +44,19 @@
 //     the same steps shifted by half a tile (PV of the previous tile first),
 //     so one wave of a SIMD feeds the matrix core while the other runs its
 //     exponentials.
-//   * The reference maximum of each row is lazy: it moves (and the
-//     accumulator is rescaled, in a branch taken by the whole wave) only when
-//     a score of the wave's rows exceeds its row's reference by more than
-//     2^8. With one reference per row used for P, l, acc and lse alike the
-//     result is the same exact softmax; P stays <= 2^8, far inside fp32 and
-//     bf16 range, and the per-tile rescale of the accumulator disappears
-//     from almost every step.
+//   * Exactness needs one reference per row used for P, l, acc and lse
+//     alike, not the true running maximum. Dense instances first run a pass
+//     in which each row's reference is the maximum of its scores in tile 0
+//     (key 0 is visible to every row) and never moves: no per-tile row
+//     maximum at all. The row sums the softmax forms anyway bound P: if a
+//     lane's share of a tile's row sum exceeds 2^40 (or is not finite), or
+//     an accumulator value is not finite at the end, the wave flags it, and
+//     the workgroup reruns the block in the checked pass.
+//     Checked pass (and the block-sparse instance): the reference is lazy,
+//     it moves (and the accumulator is rescaled, in a branch taken by the
+//     whole wave) only when a score of the wave's rows exceeds its row's
+//     reference by more than 2^8, so P <= 2^8 and the per-tile rescale of
+//     the accumulator disappears from almost every step.
 //   * Every wave runs every tile of the workgroup's key range: a tile wholly
 //     after a wave's rows is masked entirely (alpha = 1, P = 0, acc and l
 //     unchanged), which keeps the loop free of branches around the work.
@@ -61,6 +67,8 @@
 //     block index is remapped so each XCD works through whole heads (K/V of a
 //     head stay in that XCD's L2), longest causal query blocks first.
 // Scores are kept in log2 units: s2 = s * scale * log2(e), so exp is v_exp_f32.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -89,6 +97,12 @@
 // (back to 0 after them, so its PV products and the other wave's run at 0)
 #ifndef FA_FWD_PRIO_QK
 #define FA_FWD_PRIO_QK 1
+#endif
+// 1: dense instances first run a pass with a fixed per-row reference and a
+// row-sum bound check, and fall back to the checked lazy reference only for
+// blocks where the bound fails
+#ifndef FA_FWD_FAST_PASS
+#define FA_FWD_FAST_PASS 1
 #endif
 
 namespace fa {
@@ -134,11 +148,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 float* __restrict__ LSE, int N, int n_qtiles, int group, float c2,
                 const int* __restrict__ sel_row_ptr, const int* __restrict__ sel_cols, int sel_nnz) {
   using C = FwdCfg<D, NW, BN, S>;
+  constexpr bool FAST = FA_FWD_FAST_PASS && !SPARSE;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  __shared__ int redo_flag;
   FA_LDS char* lds = (FA_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // (ordered before any wave's report by the barriers of the first pass)
+  if (FAST && tid == 0) redo_flag = 0;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int h = lane >> 5;  // which 16 of each 32 keys this lane holds
   const int n = lane & 31;  // this lane's query row within the wave
@@ -219,7 +237,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Tile t goes to ring slot t % S. Past the last tile the loads repeat the
   // last tile into the (unused) slot, so every step issues the same number
   // of loads and the wait count below is a constant.
-  auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA], int k0) {
+  auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA], int k0) __attribute__((always_inline)) {
     const int slot = slot0 + (t & (S - 1));
     const char* base = (const char*)(src + (size_t)k0 * D);
     FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024;
@@ -260,7 +278,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int voff0 = tr_row * C::ROWB + 16 * (tr_chunk ^ vswz<D>(tr_row)) + 8 * (lane & 1);
 
-  float m_run = -INFINITY;  // reference maximum of s2 for row qrow (see step_head)
+  float m_run = -INFINITY;  // reference maximum of s2 for row qrow (see step_head, run)
   float l_run = 0.f;        // running sum of 2^(s2 - m_run) over this lane's keys
   f32x16_t acc[D / 32];     // O^T block: lane holds O[qrow][32j + 8(i/4) + 4h + i%4]
 #pragma unroll
@@ -275,7 +293,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto v_addr = [&](int buf) { return (int)(uintptr_t)(lds + (S + buf) * C::TILEB) + voff0; };
 
   // S^T = K Q^T for the BN keys of the K tile at LDS address kb0
-  auto qk = [&](int kb0, f32x16_t (&s)[BN / 32]) {
+  auto qk = [&](int kb0, f32x16_t (&s)[BN / 32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -293,7 +311,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // causal / tail mask of the tile starting at key k0: key j is kept iff
   // j <= qrow (causal) and j < N, i.e. (j - k0 - 4h) <= lim below
-  auto mask = [&](int k0, f32x16_t (&s)[BN / 32]) {
+  auto mask = [&](int k0, f32x16_t (&s)[BN / 32]) __attribute__((always_inline)) {
     const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -305,7 +323,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // online softmax update of one tile: new max, P (bf16), l, acc rescale.
   // Split in two so the row max can be issued ahead of the matrix work.
   // (a chain of three-input maxima: one instruction per two scores)
-  auto row_max = [&](const f32x16_t (&s)[BN / 32]) {
+  auto row_max = [&](const f32x16_t (&s)[BN / 32]) __attribute__((always_inline)) {
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int f = 2; f < BN / 2; f += 2) mx = max3(mx, s[f >> 4][f & 15], s[f >> 4][(f + 1) & 15]);
@@ -346,7 +364,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // slice by slice with the softmax of the current tile on the vector unit
   // (exponentials, row sum, bf16 rounding of P). Returns the row sum.
   auto qk_softmax = [&](int kb0, float m_use, float alpha, const f32x16_t (&s_cur)[BN / 32],
-                        f32x16_t (&s_nxt)[BN / 32], bf16x8_t (&p)[BN / 16]) {
+                        f32x16_t (&s_nxt)[BN / 32], bf16x8_t (&p)[BN / 16]) __attribute__((always_inline)) {
     bf16x8_t kr[KQ];
 #pragma unroll
     for (int i = 0; i < LA_K; ++i) kr[i] = kread(kb0, i);
@@ -400,7 +418,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // acc *= alpha, skipped when no row of the wave raised its maximum
   // (alpha = 1 on every lane: multiplying would change nothing)
-  auto rescale = [&](float alpha) {
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (FA_FWD_RESCALE_IN_SLICES) return;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
@@ -411,7 +429,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // acc += P V for the V tile at vb0
-  auto pv = [&](int vb0, const bf16x8_t (&p)[BN / 16]) {
+  auto pv = [&](int vb0, const bf16x8_t (&p)[BN / 16]) __attribute__((always_inline)) {
     bf16x8_t vr[KP];
 #pragma unroll
     for (int k = 0; k < LA_V; ++k) vr[k] = vread(vb0, k);
@@ -444,30 +462,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // K(u+2)), after which 2S-5 tiles' loads were issued, so each wave waits
   // until at most that many DMAs are outstanding, then the barrier publishes
   // the tiles to all waves.
-#pragma unroll
-  for (int t = 0; t + 2 < S; ++t) {
-    const int k0 = tile_key(t);
-    load_k(t, k0);
-    load_v(t, k0);
-  }
-  load_k(S - 2, tile_key(S - 2));
-  load_k(S - 1, tile_key(S - 1));
-  wait_loads_and_barrier<C::INFLIGHT>();
   // Block-sparse: the first keys of the tiles a step loads (u+S-2 for V, u+S
   // for K) and masks (u) come from the list; they are read one step ahead
   // (scalar loads) and passed along, so no step waits for its own list reads.
   // raw list entries of tiles u+S-2, u+S-1, u+S (loads), u (mask) and u-1
   int kw0 = 0, kw1 = 0, kw2 = 0, km = 0, km_prev = 0;
-  if constexpr (SPARSE) {
-    kw0 = list_entry(S - 2);
-    kw1 = list_entry(S - 1);
-    kw2 = list_entry(S);
-    km = list_entry(0);
-  }
-
   f32x16_t sA[BN / 32], sB[BN / 32];
   bf16x8_t pA[BN / 16], pB[BN / 16];
-  qk(k_addr(0), sA);
+
 
   // Every wave runs every step of the workgroup's key range, with no
   // branch around the work: a tile wholly after a wave's rows (or past N)
@@ -483,7 +485,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // an empty asm statement so the per-chunk XORs are formed here rather than
   // kept live across the loop), row max and alpha.
   auto step_head = [&](int u, f32x16_t (&s_cur)[BN / 32], int& kb0, int& vb0, int v_tile,
-                  float& m_use, float& alpha) {
+                  float& m_use, float& alpha, auto fast) __attribute__((always_inline)) {
     if constexpr (SPARSE) {
       const int nk = list_entry(u + S + 1), nm = list_entry(u + 1);  // for the next step
       load_v(u + S - 2, entry_key(kw0));
@@ -505,6 +507,12 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     kb0 = k_addr((u + 1) & (S - 1));
     vb0 = v_addr(v_tile & (S - 1));
     asm volatile("" : "+v"(kb0), "+v"(vb0));
+    if constexpr (decltype(fast)::value) {
+      // reference fixed for the whole pass (see run below)
+      m_use = m_run;
+      alpha = 1.f;
+      return;
+    }
     const float mx = row_max(s_cur);
 #if FA_FWD_LAZY_TAU > 0
     // Exactness does not need the true running maximum, only one reference
@@ -534,49 +542,119 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       return false;
     }
   };
+  // (fast pass: flag the wave when a lane's share of a tile's row sum
+  // exceeds 2^40 or is not finite, i.e. when some P may exceed 2^40)
+  auto overflow = [&](float lsum) { return __builtin_amdgcn_ballot_w64(!(lsum <= 0x1p40f)) != 0; };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
-                     bf16x8_t (&p)[BN / 16]) {
+                     bf16x8_t (&p)[BN / 16], auto fast, bool& bad) __attribute__((always_inline)) {
     int kb0, vb0;
     float m_use, alpha;
     const bool live = !dead(u, km);
-    step_head(u, s_cur, kb0, vb0, u, m_use, alpha);
+    step_head(u, s_cur, kb0, vb0, u, m_use, alpha, fast);
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
+    if constexpr (decltype(fast)::value) bad |= overflow(lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     if (live) pv(vb0, p);
     wait_loads_and_barrier<C::INFLIGHT>();
   };
   auto step_hi = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
-                     bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first) {
+                     bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first, auto fast,
+                     bool& bad) __attribute__((always_inline)) {
     int kb0, vb0;
     float m_use, alpha;
     const bool prev_live = !first && !dead(u - 1, km_prev);
-    step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha);
+    step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha, fast);
     if (prev_live) pv(vb0, p_prev);
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
+    if constexpr (decltype(fast)::value) bad |= overflow(lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     wait_loads_and_barrier<C::INFLIGHT>();
   };
 
-  const int n_steps = (n_tiles + 1) & ~1;
-  if (!FA_FWD_PINGPONG || w < NW / 2) {
-    for (int u = 0; u < n_steps; u += 2) {
-      step_lo(u, sA, sB, pA);
-      step_lo(u + 1, sB, sA, pB);
+  // One pass over the block's key tiles. Safe pass (fast = false): the
+  // lazy reference maximum above, checked on every tile. Fast pass (dense
+  // instances): the reference of every row is the maximum of its scores in
+  // tile 0 (which holds key 0, visible to every row, so it is finite) and
+  // never moves; no per-tile row maximum is taken. P = 2^(s2 - m_ref) stays
+  // exact for any reference; it only needs bounds so that P, l and acc stay
+  // in range, and the pass checks them through the row sums it forms anyway:
+  // a lane's share of a tile's row sum above 2^40 (or not finite), or an
+  // accumulator that is no longer finite at the end, flags the wave, and the
+  // workgroup then reruns the block in the safe pass. No wide underflow can
+  // occur: every row has P = 1 at its tile-0 maximum, so l >= 1. Returns the
+  // wave's flag.
+  auto run = [&](auto fast) __attribute__((always_inline)) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+  #pragma unroll
+    for (int t = 0; t + 2 < S; ++t) {
+      const int k0 = tile_key(t);
+      load_k(t, k0);
+      load_v(t, k0);
     }
+    load_k(S - 2, tile_key(S - 2));
+    load_k(S - 1, tile_key(S - 1));
+    wait_loads_and_barrier<C::INFLIGHT>();
+    if constexpr (SPARSE) {
+      kw0 = list_entry(S - 2);
+      kw1 = list_entry(S - 1);
+      kw2 = list_entry(S);
+      km = list_entry(0);
+    }
+    qk(k_addr(0), sA);
+    if constexpr (decltype(fast)::value) {
+      if ((CAUSAL && BN - 1 > row0) || BN > N) mask(0, sA);
+      m_run = row_max(sA) * c2;
+    }
+    bool bad = false;
+    const int n_steps = (n_tiles + 1) & ~1;
+    if (!FA_FWD_PINGPONG || w < NW / 2) {
+      for (int u = 0; u < n_steps; u += 2) {
+        step_lo(u, sA, sB, pA, fast, bad);
+        step_lo(u + 1, sB, sA, pB, fast, bad);
+      }
+    } else {
+      step_hi(0, sA, sB, pA, pB, true, fast, bad);
+      for (int u = 1; u + 1 < n_steps; u += 2) {
+        step_hi(u, sB, sA, pB, pA, false, fast, bad);
+        step_hi(u + 1, sA, sB, pA, pB, false, fast, bad);
+      }
+      step_hi(n_steps - 1, sB, sA, pB, pA, false, fast, bad);
+      // (the list entries have moved on by one step: km_prev is tile n_steps - 1's)
+      if (!dead(n_steps - 1, km_prev)) pv(v_addr((n_steps - 1) & (S - 1)), pB);
+    }
+    // no load may still be writing this workgroup's LDS when the pass ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (decltype(fast)::value) {
+      // P <= 2^40 bounds l, but acc also scales with |V|: flag the wave if
+      // any accumulator value is no longer finite
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) amax = max3(amax, fabsf(acc[j][i]), fabsf(acc[j][i + 1]));
+      bad |= __builtin_amdgcn_ballot_w64(!(amax < INFINITY)) != 0;
+    }
+    return bad;
+  };
+  if constexpr (FAST) {
+    // every wave reports, then all rerun together if any was flagged (the
+    // passes share barriers); the ring is idle: each wave has waited for its
+    // loads, and the barrier below follows every wave's last LDS read
+    const bool bad = run(std::true_type{});
+    if (bad && lane == 0) redo_flag = 1;
+    lds_barrier();
+    // (uniform: every lane reads the same word after the barrier)
+    if (__builtin_amdgcn_readfirstlane(redo_flag)) run(std::false_type{});
   } else {
-    step_hi(0, sA, sB, pA, pB, true);
-    for (int u = 1; u + 1 < n_steps; u += 2) {
-      step_hi(u, sB, sA, pB, pA, false);
-      step_hi(u + 1, sA, sB, pA, pB, false);
-    }
-    step_hi(n_steps - 1, sB, sA, pB, pA, false);
-    // (the list entries have moved on by one step: km_prev is tile n_steps - 1's)
-    if (!dead(n_steps - 1, km_prev)) pv(v_addr((n_steps - 1) & (S - 1)), pB);
+    run(std::false_type{});
   }
-  // no load may still be writing this workgroup's LDS when it exits
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = acc / l, lse = ln(2) * (m + log2 l)
   if (qrow < N) {

@@ -90,6 +90,38 @@ def test_bf16_nondefault_scale():
     _check_heads(q, k, v, o, lse, 0.37, True, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N, v_log2", [(300, 0), (777, 0), (2000, 0), (300, 110)])
+def test_bf16_rising_scores_all_rows(N, d, causal, v_log2):
+    """Scores that rise along the key index by about 4 (log2 units) per 64
+    keys, so the maxima of a row's first keys are far below those of its
+    later keys. At N = 300 the later tiles' P reach about 2^19 against the
+    first tile's maximum, which the kernel keeps as the reference; from N =
+    777 on, a tile's row sums pass 2^40 (at N = 2000 they overflow fp32) and
+    the kernel must rerun such blocks with per-tile maxima, while causal
+    blocks near the start stay below that bound, so both kinds of block occur
+    in one launch. With V scaled by 2^110 at N = 300 the accumulator, not
+    the row sum, leaves the fp32 range against the first tile's maximum
+    (about 2^135), while with per-tile maxima it stays near 2^122. Every row
+    is compared."""
+    _say("rising scores", N, d, causal, v_log2)
+    g = torch.Generator().manual_seed(77 + N + d)
+    B, H = 1, 2
+    scale = 1 / math.sqrt(d)
+    step = 4.0 / (scale * math.log2(math.e) * d)  # per 64 keys, on every component of k
+    ramp = (torch.arange(N, dtype=torch.float32) / 64 * step).view(1, 1, N, 1)
+    q = (torch.randn(B, H, N, d, generator=g) + 1.0).to(torch.bfloat16).to(DEV)
+    k = (torch.randn(B, H, N, d, generator=g) + ramp).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    # (a power-of-two factor is exact in bf16 and commutes with every
+    # rounding, so O / 2^v_log2 is compared with the oracle on the unscaled V)
+    o, lse = forward(q, k, v * 2.0**v_log2, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    _check_heads(q, k, v, o * 2.0**-v_log2, lse, scale, causal, [(0, 0), (0, 1)])
+
+
 # ---------------------------------------------------------------- configuration 2
 
 
