@@ -45,14 +45,13 @@
 //     so one wave of a SIMD feeds the matrix core while the other runs its
 //     exponentials.
 //   * Exactness needs one reference per row used for P, l, acc and lse
-//     alike, not the true running maximum. Dense instances first run a pass
-//     in which each row's reference is the maximum of its scores in tile 0
-//     (key 0 is visible to every row) and never moves: no per-tile row
-//     maximum at all. The row sums the softmax forms anyway bound P: if a
-//     lane's share of a tile's row sum exceeds 2^40 (or is not finite), or
-//     an accumulator value is not finite at the end, the wave flags it, and
-//     the workgroup reruns the block in the checked pass.
-//     Checked pass (and the block-sparse instance): the reference is lazy,
+//     alike, not the true running maximum. A block first runs a pass in
+//     which each row's reference is the maximum of its scores in the first
+//     tile and never moves: no per-tile row maximum at all. The row sums the
+//     softmax forms anyway bound P: if a lane's share of a tile's row sum
+//     exceeds 2^40 (or is not finite), or an accumulator value is not finite
+//     at the end, the wave flags it, and the workgroup reruns the block in
+//     the checked pass. Checked pass: the reference is lazy,
 //     it moves (and the accumulator is rescaled, in a branch taken by the
 //     whole wave) only when a score of the wave's rows exceeds its row's
 //     reference by more than 2^8, so P <= 2^8 and the per-tile rescale of
@@ -98,9 +97,9 @@
 #ifndef FA_FWD_PRIO_QK
 #define FA_FWD_PRIO_QK 1
 #endif
-// 1: dense instances first run a pass with a fixed per-row reference and a
-// row-sum bound check, and fall back to the checked lazy reference only for
-// blocks where the bound fails
+// 1: every block first runs a pass with a fixed per-row reference and a
+// row-sum bound check, and falls back to the checked lazy reference only
+// where the bound fails
 #ifndef FA_FWD_FAST_PASS
 #define FA_FWD_FAST_PASS 1
 #endif
@@ -148,7 +147,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 float* __restrict__ LSE, int N, int n_qtiles, int group, float c2,
                 const int* __restrict__ sel_row_ptr, const int* __restrict__ sel_cols, int sel_nnz) {
   using C = FwdCfg<D, NW, BN, S>;
-  constexpr bool FAST = FA_FWD_FAST_PASS && !SPARSE;
+  constexpr bool FAST = FA_FWD_FAST_PASS;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   __shared__ int redo_flag;
   FA_LDS char* lds = (FA_LDS char*)smem;
@@ -574,17 +573,19 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // One pass over the block's key tiles. Safe pass (fast = false): the
-  // lazy reference maximum above, checked on every tile. Fast pass (dense
-  // instances): the reference of every row is the maximum of its scores in
-  // tile 0 (which holds key 0, visible to every row, so it is finite) and
-  // never moves; no per-tile row maximum is taken. P = 2^(s2 - m_ref) stays
-  // exact for any reference; it only needs bounds so that P, l and acc stay
-  // in range, and the pass checks them through the row sums it forms anyway:
-  // a lane's share of a tile's row sum above 2^40 (or not finite), or an
-  // accumulator that is no longer finite at the end, flags the wave, and the
-  // workgroup then reruns the block in the safe pass. No wide underflow can
-  // occur: every row has P = 1 at its tile-0 maximum, so l >= 1. Returns the
-  // wave's flag.
+  // lazy reference maximum above, checked on every tile. Fast pass: the
+  // reference of every row is the maximum of its (masked) scores in the
+  // first tile and never moves; no per-tile row maximum is taken. P =
+  // 2^(s2 - m_ref) stays exact for any reference; it only needs bounds so
+  // that P, l and acc stay in range, and the pass checks them through the
+  // row sums it forms anyway: a lane's share of a tile's row sum above 2^40
+  // (or not finite), or an accumulator that is no longer finite at the end,
+  // flags the wave, and the workgroup then reruns the block in the safe
+  // pass. No wide underflow can occur: every row has P = 1 at its first-tile
+  // maximum, so l >= 1. Dense blocks start at key 0, visible to every row;
+  // a block-sparse row that sees no key of its first listed tile has
+  // reference -inf, its P are inf or NaN, and the flag catches it. Returns
+  // the wave's flag.
   auto run = [&](auto fast) __attribute__((always_inline)) {
     m_run = -INFINITY;
     l_run = 0.f;
@@ -609,7 +610,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     qk(k_addr(0), sA);
     if constexpr (decltype(fast)::value) {
-      if ((CAUSAL && BN - 1 > row0) || BN > N) mask(0, sA);
+      // (the first tile's key: the mask step_head(0) applies again)
+      const int k0 = SPARSE ? entry_key(km) : 0;
+      if (k0 + BN > N || (CAUSAL && k0 + BN - 1 > row0)) mask(k0, sA);
       m_run = row_max(sA) * c2;
     }
     bool bad = false;
