@@ -53,6 +53,12 @@ namespace {
 #ifndef FA_DEC_SLOTS128
 #define FA_DEC_SLOTS128 2
 #endif
+// Fewest workgroups a launch is split into: two per compute unit (two fit
+// in its LDS, and each adds its loads in flight); 256, 384 and 768 were 2-3 %
+// slower on the 100K-token and shared-head caches
+#ifndef FA_DEC_MIN_WG
+#define FA_DEC_MIN_WG 512
+#endif
 #ifndef FA_DEC_SLOTS64
 #define FA_DEC_SLOTS64 4
 #endif
@@ -438,9 +444,9 @@ DecodePlan decode_plan(const DecodeProblem& p) {
   const long long base = (long long)p.B * p.Hkv * pl.n_rblocks;
   // Splits of about FA_DEC_SPLIT_KEYS keys (long enough that a workgroup's
   // start-up and merge costs are small next to its stream of K and V), but
-  // at least one workgroup per compute unit, and at least 4 tiles per wave.
+  // at least FA_DEC_MIN_WG workgroups, and at least 4 tiles per wave.
   const long long tiles = ((long long)p.Nk + kDecKeys - 1) / kDecKeys;
-  long long S = std::max(((long long)p.Nk + FA_DEC_SPLIT_KEYS - 1) / FA_DEC_SPLIT_KEYS, (256 + base - 1) / base);
+  long long S = std::max(((long long)p.Nk + FA_DEC_SPLIT_KEYS - 1) / FA_DEC_SPLIT_KEYS, (FA_DEC_MIN_WG + base - 1) / base);
   S = std::max(1LL, std::min(S, tiles / (kDecodeWaves * 4)));
   const long long step = (long long)kDecKeys * kDecodeWaves;
   long long L = ((p.Nk + S - 1) / S + step - 1) / step * step;
