@@ -593,7 +593,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int j = 0; j < D / 32; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t + 2 < S; ++t) {
       const int k0 = tile_key(t);
       load_k(t, k0);
