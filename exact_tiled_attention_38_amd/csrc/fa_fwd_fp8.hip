@@ -59,6 +59,9 @@ namespace {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
+#ifndef FA_FP8_SUMCHECK
+#define FA_FP8_SUMCHECK 1
+#endif
 constexpr float kP8Tau = 4.f;    // reference moves when a score exceeds it by 2^4
 constexpr float kP8Shift = 4.f;  // P = 2^(s - m_ref + 4) <= 2^8
 
@@ -323,6 +326,12 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
 #pragma unroll
   for (int i = 0; i < BN / 64; ++i) pA[i] = pB[i] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   qk(k_base(0), sA);
+  if constexpr (FA_FP8_SUMCHECK) {
+    // key 0 is visible to every row: the first tile's masked maximum is a
+    // finite initial reference (step_head(0) applies the same mask again)
+    if ((CAUSAL && BN - 1 > row0) || BN > N) mask(0, sA);
+    m_run = row_max(sA) * c2;
+  }
 
   auto step_head = [&](int u, f32x16_t (&s_cur)[BN / 32], int& kb0, int& vb0, int v_tile, float& m_use,
                        float& alpha) {
@@ -333,6 +342,12 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     kb0 = k_base((u + 1) & (S - 1));
     vb0 = v_base(v_tile & (S - 1));
     asm volatile("" : "+v"(kb0), "+v"(vb0));
+    if constexpr (FA_FP8_SUMCHECK) {
+      // the reference only moves in check() below
+      m_use = m_run - kP8Shift;
+      alpha = 1.f;
+      return;
+    }
     const float mx = row_max(s_cur);
     const bool move = __builtin_amdgcn_ballot_w64(mx * c2 > m_run + kP8Tau) != 0;
     const float m_new = move ? fmaxf(m_run, mx * c2) : m_run;
@@ -340,11 +355,45 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     alpha = exp2_fast((m_run - kP8Shift) - m_use);
     m_run = m_new;
   };
+  // Row-sum check: P of a tile is formed with the row's current reference;
+  // a lane's share of the tile's row sum of at most 2^8 bounds every P by
+  // 2^8 (as the lazy rule does; e4m3 holds up to 448). Otherwise (rare: a
+  // score well above the reference) the wave takes the tile's row maxima,
+  // moves each row's reference to its maximum, rescales l and acc, and forms
+  // the tile's P again. The reference is always a score the row has seen,
+  // so the largest P of a row is at least 2^4, as with the lazy rule.
+  auto check = [&](const f32x16_t (&s_cur)[BN / 32], i32x8_t (&p)[BN / 64], float& lsum) {
+    if constexpr (FA_FP8_SUMCHECK) {
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= 256.f))) {
+        const float mx = row_max(s_cur);
+        const float m_new = fmaxf(m_run, mx * c2);
+        const float a = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= a;
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][e] *= a;
+        const float m_use = m_new - kP8Shift;
+        lsum = 0.f;
+#pragma unroll
+        for (int f = 0; f < BN / 2; f += 2) {
+          const float p0 = exp2_fast(fmaf(s_cur[f >> 4][f & 15], c2, -m_use));
+          const float p1 = exp2_fast(fmaf(s_cur[f >> 4][(f + 1) & 15], c2, -m_use));
+          lsum += p0 + p1;
+          const int kc = f >> 5, byte = f & 31;
+          if (byte & 2) p[kc][byte >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, p[kc][byte >> 2], true);
+          else p[kc][byte >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, p[kc][byte >> 2], false);
+        }
+      }
+    }
+  };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32], i32x8_t (&p)[BN / 64]) {
     int kb0, vb0;
     float m_use, alpha;
     step_head(u, s_cur, kb0, vb0, u, m_use, alpha);
-    const float lsum = qk_softmax(kb0, m_use, s_cur, s_nxt, p);
+    float lsum = qk_softmax(kb0, m_use, s_cur, s_nxt, p);
+    check(s_cur, p, lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     pv(vb0, p);
@@ -356,7 +405,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     float m_use, alpha;
     step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha);
     if (!first) pv(vb0, p_prev);
-    const float lsum = qk_softmax(kb0, m_use, s_cur, s_nxt, p_cur);
+    float lsum = qk_softmax(kb0, m_use, s_cur, s_nxt, p_cur);
+    check(s_cur, p_cur, lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     wait_loads_and_barrier<C::INFLIGHT>();
