@@ -110,6 +110,32 @@ def test_fp8_sharp_rows_and_large_values():
                     o[0, h].float().cpu().numpy(), lse[0, h].cpu().numpy(), 0.2, True, what=f"head {h}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_rising_scores(causal):
+    """Scores that climb by about 3 (log2 units) per 64 keys, so later tiles
+    pass a row's reference by more than 4 and the kernel must move it in the
+    middle of a row (a tile's row sums then exceed 2^8); every row checked."""
+    _say("fp8 rising scores", causal)
+    B, H, N, d = 1, 2, 700, 128
+    g = torch.Generator().manual_seed(6300 + causal)
+    scale = 1 / math.sqrt(d)
+    step = 3.0 / (scale * math.log2(math.e) * d)
+    ramp = (torch.arange(N, dtype=torch.float32) / 64 * step).view(1, 1, N, 1)
+    xs = [torch.randn(B, H, N, d, generator=g) + 1.0, torch.randn(B, H, N, d, generator=g) + ramp,
+          torch.randn(B, H, N, d, generator=g)]
+    codes, factors = [], []
+    for x in xs:
+        f = float(x.abs().max()) / 448.0
+        codes.append((x / f).to(torch.float8_e4m3fn).to(DEV))
+        factors.append(f)
+    q, k, v = codes
+    o, lse = forward_fp8(q, k, v, *factors, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for h in range(H):
+        _check_head(_codes(q[0, h]), _codes(k[0, h]), _codes(v[0, h]), *factors,
+                    o[0, h].float().cpu().numpy(), lse[0, h].cpu().numpy(), scale, causal, what=f"head {h}")
+
+
 def test_fp8_deterministic():
     _say("fp8 determinism")
     (q, k, v), f = W.make_fp8_inputs(dict(seed=6200), DEV, shape=(2, 4, 1000, 128))
