@@ -36,6 +36,12 @@
 namespace fa {
 namespace {
 
+// 1: the dP products start from D and V is negated, so the softmax gradient
+// needs no subtraction per score
+#ifndef FA_BWD_DFOLD
+#define FA_BWD_DFOLD 1
+#endif
+
 constexpr int kBwdWaves = 4;
 constexpr int kBwdKeys = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdRows = 64;              // query rows per tile
@@ -150,6 +156,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) asm volatile("" :: "v"(kf[c]), "v"(vf[c]));
   __builtin_amdgcn_s_waitcnt(0);
+#if FA_BWD_DFOLD
+  // V enters dP only: negated once here (bf16 sign bits), the dP products
+  // start from the rows' D and so yield D - dP directly (see grad_pair)
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    u32x4_t x = __builtin_bit_cast(u32x4_t, vf[c]);
+    x ^= 0x80008000u;
+    vf[c] = __builtin_bit_cast(bf16x8_t, x);
+  }
+#endif
 
   f32x16_t dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
@@ -261,13 +277,28 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         st_d[qb][g] = *(const FA_LDS f32x4_t*)&rowstat[slot][1][qb * 32 + 8 * g + 4 * h];
       }
     };
+    // the accumulator a dP product chain starts from: the rows' D in the
+    // accumulator's layout (element i: row 8(i/4) + 4h + i%4), or 0
+    auto dinit = [&](int qb) {
+      f32x16_t r = {};
+#if FA_BWD_DFOLD
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = st_d[qb][i >> 2][i & 3];
+#endif
+      return r;
+    };
     // P and dS (bf16) for elements 2pr, 2pr+1 of block qb
     auto grad_pair = [&](int qb, int pr) {
       const int i = 2 * pr, g = i >> 2, e = i & 3;
       const float p0 = exp2_fast(fmaf(s[qb][i], c2, -st_l[qb][g][e]));
       const float p1 = exp2_fast(fmaf(s[qb][i + 1], c2, -st_l[qb][g][e + 1]));
       const bf16x2_t pp = to_bf16x2(p0, p1);
+#if FA_BWD_DFOLD
+      // dp holds D - dP: dS = P (dP - D) = -P (D - dP)
+      const bf16x2_t dd = to_bf16x2(p0 * -dp[qb][i], p1 * -dp[qb][i + 1]);
+#else
       const bf16x2_t dd = to_bf16x2(p0 * (dp[qb][i] - st_d[qb][g][e]), p1 * (dp[qb][i + 1] - st_d[qb][g][e + 1]));
+#endif
       pb[qb][i >> 3][i & 7] = pp[0];
       pb[qb][i >> 3][(i & 7) + 1] = pp[1];
       dsb[qb][i >> 3][i & 7] = dd[0];
@@ -287,6 +318,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
     bf16x8_t ra[NC], rg[NC];
     read_stats(0);
+#if FA_BWD_DFOLD
+    read_stats(1);  // (block 1's D seeds its dP products in A1)
+#endif
     ra[0] = rread(Qs, 0, 0); rg[0] = rread(Gs, 0, 0);
     ra[1] = rread(Qs, 0, 1); rg[1] = rread(Gs, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -298,12 +332,14 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       else { ra[cn - NC] = rread(Qs, 1, cn - NC); rg[cn - NC] = rread(Gs, 1, cn - NC); }
       const f32x16_t z = {};
       s[0] = mfma_32x32x16(ra[c], kf[c], c == 0 ? z : s[0]);
-      dp[0] = mfma_32x32x16(rg[c], vf[c], c == 0 ? z : dp[0]);
+      dp[0] = mfma_32x32x16(rg[c], vf[c], c == 0 ? dinit(0) : dp[0]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (need_mask) mask(0);
     // A1 with the softmax gradient of block 0
+#if !FA_BWD_DFOLD
     read_stats(1);
+#endif
     bf16x8_t ta[NB], tg[NB];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -312,7 +348,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       else { ta[cn - NC] = tread(Qs, 0, cn - NC); tg[cn - NC] = tread(Gs, 0, cn - NC); }
       const f32x16_t z = {};
       s[1] = mfma_32x32x16(ra[c], kf[c], c == 0 ? z : s[1]);
-      dp[1] = mfma_32x32x16(rg[c], vf[c], c == 0 ? z : dp[1]);
+      dp[1] = mfma_32x32x16(rg[c], vf[c], c == 0 ? dinit(1) : dp[1]);
 #pragma unroll
       for (int pr = c * (8 - K0) / NC; pr < (c + 1) * (8 - K0) / NC; ++pr) grad_pair(0, pr);
       __builtin_amdgcn_sched_barrier(0);
