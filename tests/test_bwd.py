@@ -114,6 +114,34 @@ def test_backward_sharp_softmax_rows(q_mult, scale):
             assert np.all(err <= bound), f"{name} head {(b, h)}: worst err/bound {(err / bound).max():.2f}"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_rising_scores(causal):
+    """Scores that climb by about 4 (log2 units) per 64 keys (the forward's
+    fixed-reference pass reruns such blocks), so lse grows along the rows and
+    the late keys dominate. O and lse come from the library's forward; the
+    bound is the plain rule plus twice the first-order bf16 rounding bounds,
+    as for the sharp rows above."""
+    _say("bwd rising scores", causal)
+    B, H, N, d = 1, 2, 777, 128
+    g = torch.Generator().manual_seed(91 + causal)
+    scale = 1 / math.sqrt(d)
+    step = 4.0 / (scale * math.log2(math.e) * d)
+    ramp = (torch.arange(N, dtype=torch.float32) / 64 * step).view(1, 1, N, 1)
+    q = (torch.randn(B, H, N, d, generator=g) + 1.0).to(torch.bfloat16).to(DEV)
+    k = (torch.randn(B, H, N, d, generator=g) + ramp).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    _, _, dq, dk, dv = _run(q, k, v, do, causal, scale)
+    for b, h in [(0, 0), (0, 1)]:
+        qh, kh, vh, doh = host(q[b, h]), host(k[b, h]), host(v[b, h]), host(do[b, h])
+        dq_ref, dk_ref, dv_ref, _, _ = oracle.backward(qh, kh, vh, doh, scale, causal)
+        extra = bf16_first_order_bounds(qh, kh, vh, doh, scale, causal)
+        for name, got, ref in (("dv", dv, dv_ref), ("dk", dk, dk_ref), ("dq", dq, dq_ref)):
+            err = np.abs(host(got[b, h]) - ref)
+            bound = GRAD_ATOL + GRAD_RTOL * np.abs(ref) + 2 * extra[name]
+            assert np.all(err <= bound), f"{name} head {(b, h)}: worst err/bound {(err / bound).max():.2f}"
+
+
 def test_config5_sampled_heads():
     cfg = W.config(5)
     _say("config 5", cfg["name"])
