@@ -542,8 +542,18 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
   // (fast pass: flag the wave when a lane's share of a tile's row sum
-  // exceeds 2^40 or is not finite, i.e. when some P may exceed 2^40)
-  auto overflow = [&](float lsum) { return __builtin_amdgcn_ballot_w64(!(lsum <= 0x1p40f)) != 0; };
+  // exceeds 2^40 or is not finite, i.e. when some P may exceed 2^40.) The
+  // test is on the bit pattern: the sum is never negative, so as an unsigned
+  // integer every value above 2^40 (0x53800000), +inf and every NaN of
+  // either sign lies above that of 2^40. This file is built without NaN
+  // semantics, where a float compare may not see a NaN, and the compiler
+  // turns some bit tests back into float compares: the empty asm makes the
+  // bit pattern an opaque integer, so the test stays an integer compare.
+  auto overflow = [&](float lsum) {
+    uint32_t bits = __float_as_uint(lsum);
+    asm volatile("" : "+v"(bits));
+    return __builtin_amdgcn_ballot_w64(bits > 0x53800000u) != 0;
+  };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p)[BN / 16], auto fast, bool& bad) __attribute__((always_inline)) {
     int kb0, vb0;
@@ -583,9 +593,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // flags the wave, and the workgroup then reruns the block in the safe
   // pass. No wide underflow can occur: every row has P = 1 at its first-tile
   // maximum, so l >= 1. Dense blocks start at key 0, visible to every row;
-  // a block-sparse row that sees no key of its first listed tile has
-  // reference -inf, its P are inf or NaN, and the flag catches it. Returns
-  // the wave's flag.
+  // a block-sparse row that sees no key of its first listed tile has no
+  // finite reference, and the wave is flagged at once. Returns the wave's
+  // flag.
   auto run = [&](auto fast) __attribute__((always_inline)) {
     m_run = -INFINITY;
     l_run = 0.f;
@@ -609,13 +619,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       km = list_entry(0);
     }
     qk(k_addr(0), sA);
+    bool bad = false;
     if constexpr (decltype(fast)::value) {
       // (the first tile's key: the mask step_head(0) applies again)
       const int k0 = SPARSE ? entry_key(km) : 0;
       if (k0 + BN > N || (CAUSAL && k0 + BN - 1 > row0)) mask(k0, sA);
       m_run = row_max(sA) * c2;
+      // (an ordered compare: no NaN semantics needed)
+      bad = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     }
-    bool bad = false;
     const int n_steps = (n_tiles + 1) & ~1;
     if (!FA_FWD_PINGPONG || w < NW / 2) {
       for (int u = 0; u < n_steps; u += 2) {
@@ -636,13 +648,20 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (decltype(fast)::value) {
       // P <= 2^40 bounds l, but acc also scales with |V|: flag the wave if
-      // any accumulator value is no longer finite
-      float amax = 0.f;
+      // any accumulator value is no longer finite. A sum of the magnitudes
+      // is inf or NaN if any term is (additions propagate NaN in every
+      // floating-point mode, where a maximum may drop it; a finite sum that
+      // overflows only costs a rerun); then the exponent bits of the sum
+      // are tested, all ones meaning inf or NaN.
+      float asum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < D / 32; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) amax = max3(amax, fabsf(acc[j][i]), fabsf(acc[j][i + 1]));
-      bad |= __builtin_amdgcn_ballot_w64(!(amax < INFINITY)) != 0;
+        for (int i = 0; i < 16; ++i) asum[i & 3] += fabsf(acc[j][i]);
+      // (opaque integer, as in overflow() above)
+      uint32_t bits = __float_as_uint((asum[0] + asum[1]) + (asum[2] + asum[3]));
+      asm volatile("" : "+v"(bits));
+      bad |= __builtin_amdgcn_ballot_w64((bits & 0x7f800000u) == 0x7f800000u) != 0;
     }
     return bad;
   };

@@ -364,7 +364,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
   // so the largest P of a row is at least 2^4, as with the lazy rule.
   auto check = [&](const f32x16_t (&s_cur)[BN / 32], i32x8_t (&p)[BN / 64], float& lsum) {
     if constexpr (FA_FP8_SUMCHECK) {
-      if (__builtin_amdgcn_ballot_w64(!(lsum <= 256.f))) {
+      // (on the bit pattern: the sum is never negative, so every value
+      // above 2^8 (0x43800000), +inf and every NaN compare above it as
+      // unsigned integers; this file is built without NaN semantics, and
+      // the empty asm makes the pattern an opaque integer, so the compiler
+      // cannot turn the test back into a float compare)
+      uint32_t lbits = __float_as_uint(lsum);
+      asm volatile("" : "+v"(lbits));
+      if (__builtin_amdgcn_ballot_w64(lbits > 0x43800000u)) {
         const float mx = row_max(s_cur);
         const float m_new = fmaxf(m_run, mx * c2);
         const float a = exp2_fast(m_run - m_new);

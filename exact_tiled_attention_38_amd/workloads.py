@@ -264,3 +264,55 @@ def decode_probe_index(o):
     bits = torch.round(o[..., :PROBE_BITS].float()).to(torch.int64)
     weights = (1 << torch.arange(PROBE_BITS, device=o.device, dtype=torch.int64))
     return (bits * weights).sum(-1)
+
+
+# Probes with shared key/value heads and with queries at the end of a longer
+# key sequence (decode). Key/value head g numbers its keys through the
+# permutation r_g(j) = (j + off_g) mod Nk, off_g = 37 g mod Nk: the max and
+# min probes' K_j spells r_g(j) (so s_ij = +-32 r_g(j) exactly), V_j spells
+# the key index j in its first PROBE_BITS columns, and column PROBE_BITS of V
+# holds g + 1. The row's output then spells the key index that maximises (or
+# minimises) r_g over the row's visible keys, and its column PROBE_BITS reads
+# g + 1: both the K and the V head of every query head are pinned exactly.
+# The count probe is as above (Q = 0, V = 1), with column PROBE_BITS of V
+# also g + 1, which every visible key then contributes with weight exactly 1.
+
+def probe_key_order(g, Nk):
+    """r_g(j) for j in range(Nk), as an int64 numpy array (a permutation of range(Nk))."""
+    off = (37 * g) % Nk
+    return (np.arange(Nk, dtype=np.int64) + off) % Nk
+
+
+def probe_heads_inputs(kind, B, H, Hkv, Nq, Nk, d, device, dtype=torch.bfloat16, rotate=True):
+    """(q [B, H, Nq, d], k [B, Hkv, Nk, d], v [B, Hkv, Nk, d]) for the shared-head probes above
+    (rotate=False: r_g(j) = j for every head)."""
+    if d <= PROBE_BITS:
+        raise ValueError("probe needs d > PROBE_BITS")
+    j = torch.arange(Nk, device=device, dtype=torch.int64)
+    q = torch.zeros((Nq, d), device=device, dtype=torch.float32)
+    if kind in ("max", "min"):
+        sign = 1.0 if kind == "max" else -1.0
+        q[:, 0], q[:, 1], q[:, 2] = sign * 32 * 4096, sign * 32 * 64, sign * 32
+    elif kind != "count":
+        raise ValueError(kind)
+    ks, vs = [], []
+    for g in range(Hkv):
+        k = torch.zeros((Nk, d), device=device, dtype=torch.float32)
+        v = torch.zeros((Nk, d), device=device, dtype=torch.float32)
+        if kind == "count":
+            k.normal_(generator=torch.Generator(device=device).manual_seed(7 + g))
+            v[:, :PROBE_BITS] = 1.0
+        else:
+            r = torch.as_tensor(probe_key_order(g if rotate else 0, Nk), device=device)
+            k[:, 0] = ((r // 4096) % 64).float()
+            k[:, 1] = ((r // 64) % 64).float()
+            k[:, 2] = (r % 64).float()
+            for bit in range(PROBE_BITS):
+                v[:, bit] = ((j >> bit) & 1).float()
+        v[:, PROBE_BITS] = float(g + 1)
+        ks.append(k)
+        vs.append(v)
+    qq = q.to(dtype).expand(B, H, Nq, d).contiguous()
+    kk = torch.stack(ks).to(dtype).expand(B, Hkv, Nk, d).contiguous()
+    vv = torch.stack(vs).to(dtype).expand(B, Hkv, Nk, d).contiguous()
+    return qq, kk, vv

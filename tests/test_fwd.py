@@ -92,7 +92,7 @@ def test_bf16_nondefault_scale():
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N, v_log2", [(300, 0), (777, 0), (2000, 0), (300, 110)])
+@pytest.mark.parametrize("N, v_log2", [(300, 0), (777, 0), (2000, 0), (300, 110), (500, 100)])
 def test_bf16_rising_scores_all_rows(N, d, causal, v_log2):
     """Scores that rise along the key index by about 4 (log2 units) per 64
     keys, so the maxima of a row's first keys are far below those of its
@@ -103,8 +103,12 @@ def test_bf16_rising_scores_all_rows(N, d, causal, v_log2):
     blocks near the start stay below that bound, so both kinds of block occur
     in one launch. With V scaled by 2^110 at N = 300 the accumulator, not
     the row sum, leaves the fp32 range against the first tile's maximum
-    (about 2^135), while with per-tile maxima it stays near 2^122. Every row
-    is compared."""
+    (about 2^135), while with per-tile maxima it stays near 2^122. At N =
+    500 with V of about +-2^100 (1e30, random signs) P reaches about 2^35
+    against the first tile's maximum, below the row-sum bound, but single
+    products reach 2^137: accumulators overflow with both signs and become
+    NaN (inf - inf) rather than inf, which the kernel must flag as well; the
+    oracle's O is finite. Every row is compared."""
     _say("rising scores", N, d, causal, v_log2)
     g = torch.Generator().manual_seed(77 + N + d)
     B, H = 1, 2
