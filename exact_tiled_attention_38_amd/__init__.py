@@ -6,9 +6,10 @@ thin Python binding: it checks tensors, allocates outputs with PyTorch and
 passes device pointers and the current stream to the library.
 """
 
-from .api import (SPARSE_BLOCK_M, SPARSE_BLOCK_N, backward, backward_workspace_bytes, decode,
-                  decode_workspace_bytes, forward, forward_block_sparse, forward_f32, forward_fp8, merge,
-                  status_string)
+from .api import (DECODE_SCRATCH_BYTES, SPARSE_BLOCK_M, SPARSE_BLOCK_N, backward, backward_workspace_bytes,
+                  decode, decode_noalloc, decode_workspace_bytes, forward, forward_block_sparse, forward_f32,
+                  forward_fp8, merge, status_string)
 
 __all__ = ["forward", "forward_f32", "forward_fp8", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
-           "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]
+           "decode_workspace_bytes", "decode_noalloc", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N",
+           "DECODE_SCRATCH_BYTES"]

@@ -29,6 +29,7 @@ SIGNATURES = {
     "fa_backward_gqa": (_i, [_p] * 10 + [_i, _i, _i, _i, _i, _i, _f, _p]),
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_i] * 6),
     "fa_decode": (_i, [_p] * 6 + [_i] * 7 + [_f, _p]),
+    "fa_decode_noalloc": (_i, [_p] * 5 + [_i] * 7 + [_f, _p]),
     "fa_merge": (_i, [_p] * 4 + [_i, ctypes.c_longlong, _i, _p]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
 }

@@ -13,7 +13,7 @@ import torch
 from . import _lib
 
 __all__ = ["forward", "forward_f32", "forward_fp8", "forward_block_sparse", "backward", "backward_workspace_bytes", "decode",
-           "decode_workspace_bytes", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]
+           "decode_workspace_bytes", "decode_noalloc", "DECODE_SCRATCH_BYTES", "merge", "status_string", "SPARSE_BLOCK_M", "SPARSE_BLOCK_N"]
 
 # Block sizes of the block-sparse selection (FA_SPARSE_BLOCK_M / _N in include/fa.h).
 SPARSE_BLOCK_M = 256
@@ -180,6 +180,36 @@ def decode(q, k, v, causal=False, scale=None, workspace=None, out=None, lse=None
     )
     _lib.check(rc, "fa_decode")
     return o, l
+
+
+# Largest decode workspace the allocation-free decode can hold
+# (FA_DECODE_SCRATCH_BYTES in include/fa.h).
+DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q, k, v, out, lse, causal=False, scale=None):
+    """decode() into preallocated `out` and `lse`, with no device allocation by
+    the library or this binding: the key-split partials live in the library's
+    static per-device scratch (DECODE_SCRATCH_BYTES; larger problems raise).
+    Calls that may overlap on one GPU race on that scratch. Returns (out, lse)."""
+    B, H, Nq, d = _check([q], ["q"], torch.bfloat16)
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k must be [B, Hkv, Nk, d] with B={B}, d={d}; got {tuple(k.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"k/v have {Hkv} heads, which must divide q's {H} heads")
+    _check([k, v], ["k", "v"], torch.bfloat16, (B, Hkv, Nk, d))
+    _check([out], ["out"], torch.bfloat16, (B, H, Nq, d))
+    _check([lse], ["lse"], torch.float32, (B, H, Nq))
+    for t, n in ((k, "k"), (out, "out"), (lse, "lse")):
+        if t.device != q.device:
+            raise ValueError(f"{n} is on {t.device}, expected {q.device}")
+    rc = _lib.lib().fa_decode_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, Hkv, Nq, Nk, d, int(bool(causal)), _scale(scale, d), _stream(q),
+    )
+    _lib.check(rc, "fa_decode_noalloc")
+    return out, lse
 
 
 def merge(o_parts, lse_parts):

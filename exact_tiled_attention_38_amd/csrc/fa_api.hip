@@ -185,6 +185,19 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   return launch_status(fa::launch_decode(q, k, v, o, lse, workspace, p, stream));
 }
 
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                      int Nq, int Nk, int d, int causal, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  const int s = check_decode(B, H, Hkv, Nq, Nk, d, causal, scale);
+  if (s != FA_OK) return s;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const fa::DecodeProblem p{B, H, Hkv, Nq, Nk, d, causal, scale};
+  if (fa::decode_workspace_bytes(p) > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+  return launch_status(fa::launch_decode_noalloc(q, k, v, o, lse, p, stream));
+}
+
 int fa_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int S, long long rows,
              int d, hipStream_t stream) {
   if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
@@ -206,6 +219,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be positive and finite";
     case FA_ERR_LAUNCH: return g_launch_error;
+    case FA_ERR_SCRATCH:
+      return "the call needs more than the library's static scratch (FA_DECODE_SCRATCH_BYTES; "
+             "fa_decode_workspace_bytes gives the need): use fa_decode with a workspace";
     default: return "unknown status";
   }
 }

@@ -39,12 +39,28 @@
 //     workspace; a second kernel merges the splits.
 // Scores are kept in log2 units inside the kernel (s2 = s * scale * log2 e).
 #include <algorithm>
+#include <mutex>
 
+#include "fa.h"
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
+
+static_assert(FA_DECODE_SCRATCH_BYTES == kDecodeScratchBytes, "scratch size of the header and the library");
+
+// Scratch of the no-allocation decode entry point (partial O and lse of the
+// key splits, as the caller's workspace holds them otherwise). Every GPU the
+// library runs on holds its own copy until the process ends. In host code
+// this name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, per device, below.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 // Keys per split (about 2 MB of K and V at d = 128) and ring slots per wave.
 #ifndef FA_DEC_SPLIT_KEYS
@@ -468,6 +484,32 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
                     : launch_decode_t<128, NW, FA_DEC_SLOTS128, false>(q, k, v, o, lse, workspace, p, stream);
   return p.causal ? launch_decode_t<64, NW, FA_DEC_SLOTS64, true>(q, k, v, o, lse, workspace, p, stream)
                   : launch_decode_t<64, NW, FA_DEC_SLOTS64, false>(q, k, v, o, lse, workspace, p, stream);
+}
+
+hipError_t decode_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current: its copy's address
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const DecodeProblem& p, hipStream_t stream) {
+  void* ws = nullptr;
+  const hipError_t e = decode_scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // (the kernels write every partial before the merge reads it: nothing to clear)
+  return launch_decode(q, k, v, o, lse, ws, p, stream);
 }
 
 hipError_t launch_merge_bf16(const void* o_parts, const float* lse_parts, void* o, float* lse, int S,

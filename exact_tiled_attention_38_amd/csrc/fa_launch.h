@@ -71,6 +71,12 @@ DecodePlan decode_plan(const DecodeProblem& p);
 size_t decode_workspace_bytes(const DecodeProblem& p);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                          const DecodeProblem& p, hipStream_t stream);
+// Decode with its partials in the library's static per-device scratch
+// (kDecodeScratchBytes; the caller checks the size first) instead of a
+// caller workspace: no allocation of any kind.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const DecodeProblem& p, hipStream_t stream);
 // Merge of S bf16 partial outputs [S][rows][d] with their lse [S][rows].
 hipError_t launch_merge_bf16(const void* o_parts, const float* lse_parts, void* o, float* lse, int S,
                              long long rows, int d, hipStream_t stream);

@@ -49,7 +49,9 @@
  *     0 < scale < inf; B*H*N*d < 2^62, and every kernel grid below 2^32
  *     work-items: B*H*ceil(N/256)*512, B*H*ceil(N/64)*64 and B*H*N*d/8
  *     each < 2^32 (at N = 16384, d = 128: B*H < 16384).
- *   - Thread safety: stateless apart from a per-thread error string.
+ *   - Thread safety: stateless apart from a per-thread error string and,
+ *     for fa_decode_noalloc, a lock-guarded per-device address of its
+ *     static scratch (whose contents calls on one GPU share).
  *   - Determinism: forward and backward outputs are bitwise reproducible run
  *     to run (no atomics anywhere).
  */
@@ -71,7 +73,9 @@ enum {
   FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or causal not in {0, 1}          */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
   FA_ERR_SCALE = 5,       /* scale is not positive, or NaN or infinite           */
-  FA_ERR_LAUNCH = 6       /* the HIP kernel launch itself failed                  */
+  FA_ERR_LAUNCH = 6,      /* the HIP kernel launch itself failed                  */
+  FA_ERR_SCRATCH = 7      /* fa_decode_noalloc: the call needs more than the
+                             static scratch (FA_DECODE_SCRATCH_BYTES)            */
 };
 
 /*
@@ -232,6 +236,26 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
               int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
               hipStream_t stream);
+
+/*
+ * fa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid allocation.
+ * Same arguments as fa_decode without the workspace, same kernels and the
+ * same results bit for bit; the split partials live instead in one static
+ * scratch array of FA_DECODE_SCRATCH_BYTES inside the library, of which
+ * every GPU the library runs on holds its own copy until the process ends.
+ * The call allocates and frees nothing (its first call on a device looks up
+ * that device's copy of the array, with the device current).
+ *   Sizes whose fa_decode_workspace_bytes exceeds FA_DECODE_SCRATCH_BYTES
+ *   return FA_ERR_SCRATCH before any HIP call; other checks as fa_decode.
+ *   All calls on one GPU share its scratch: calls that may overlap on one
+ *   GPU (other streams, other threads) race and give wrong results; calls
+ *   ordered on one stream are safe, each overwriting the last one's partials.
+ */
+#define FA_DECODE_SCRATCH_BYTES (32u << 20)
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                      hipStream_t stream);
 
 /*
  * Merge S partial attention results computed over disjoint sets of keys

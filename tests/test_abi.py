@@ -40,7 +40,7 @@ def L():
 def test_status_enum_matches_documentation():
     assert CODES == {
         "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_UNSUPPORTED": 3,
-        "FA_ERR_ALIGN": 4, "FA_ERR_SCALE": 5, "FA_ERR_LAUNCH": 6,
+        "FA_ERR_ALIGN": 4, "FA_ERR_SCALE": 5, "FA_ERR_LAUNCH": 6, "FA_ERR_SCRATCH": 7,
     }
 
 
@@ -297,3 +297,19 @@ def test_fp8_rejects_invalid_arguments(L, kw, code):
     rc = L.fa_forward_fp8(*args, f(kw.get("qd", 1.0)), f(kw.get("kd", 1.0)), f(kw.get("vd", 1.0)), 1, 4,
                           kw.get("Hkv", 4), 256, kw.get("d", 128), 1, f(kw.get("scale", 0.125)), None)
     assert rc == CODES[code]
+
+
+def test_decode_noalloc_error_paths(L):
+    """fa_decode_noalloc checks its arguments as fa_decode does, and rejects
+    problems whose partials exceed the static scratch, all before any HIP call."""
+    A = 1 << 12
+    call = lambda ptrs, B=1, H=8, Hkv=8, Nq=1, Nk=1000, d=128, causal=1: L.fa_decode_noalloc(
+        *ptrs, B, H, Hkv, Nq, Nk, d, causal, ctypes.c_float(0.1), None)
+    assert call([0, A, A, A, A]) == CODES["FA_ERR_NULL"]
+    assert call([A, A, A, A, 0]) == CODES["FA_ERR_NULL"]
+    assert call([A] * 5, Hkv=3) == CODES["FA_ERR_SHAPE"]
+    assert call([A] * 5, d=96) == CODES["FA_ERR_UNSUPPORTED"]
+    assert call([A] * 5, Nq=5, Nk=4) == CODES["FA_ERR_SHAPE"]
+    assert call([A + 8] + [A] * 4) == CODES["FA_ERR_ALIGN"]
+    assert call([A] * 5, B=8, H=32, Hkv=32, Nq=4, Nk=200000) == CODES["FA_ERR_SCRATCH"]
+    assert "static scratch" in _lib.status_string(CODES["FA_ERR_SCRATCH"])
