@@ -22,6 +22,11 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+# Race-check build (tests only): the same library with the bf16 forward
+# compiled with -DFA_SAFE_SYNC=1 (every load waited for, a barrier after each
+# LDS phase); its forward must match libfa.so's bit for bit.
+SAFE_LIB = os.path.join(PKG, "libfa_safe.so")
+SAFE_SOURCES = {"fa_fwd_bf16.hip": "fa_fwd_bf16_safe"}
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_bwd_dq.hip", "fa_decode.hip",
            "fa_fwd_fp8.hip"]
 # The bf16 forward's row max runs on v_max_f32 without the IEEE-mode NaN
@@ -54,12 +59,12 @@ def common_flags(extra=()):
     ]
 
 
-def _compile(src, extra, keep_asm):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra, keep_asm, stem=None):
+    obj = os.path.join(BUILD_DIR, (stem or os.path.splitext(src)[0]) + ".o")
     flags = [*common_flags(extra), *PER_FILE_FLAGS.get(src, [])]
     cmd = [hipcc(), *flags, "-c", os.path.join(HERE, src), "-o", obj]
     if keep_asm:
-        asm = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + "-gfx950.s")
+        asm = os.path.join(BUILD_DIR, (stem or os.path.splitext(src)[0]) + "-gfx950.s")
         subprocess.run([hipcc(), *flags, "--cuda-device-only", "-S", os.path.join(HERE, src), "-o", asm],
                        cwd=BUILD_DIR, capture_output=True, text=True)
     r = subprocess.run(cmd, cwd=BUILD_DIR, capture_output=True, text=True)
@@ -70,22 +75,36 @@ def _compile(src, extra, keep_asm):
     return obj, err
 
 
-def build(extra=(), keep_asm=False, verbose=False):
-    """Compile every HIP source and link libfa.so. Always recompiles."""
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    # (-Bsymbolic: the library's own calls bind inside it, so the race-check
+    # library can be loaded beside libfa.so in one process)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(extra=(), keep_asm=False, verbose=False, safe=True):
+    """Compile every HIP source and link libfa.so (and, with safe, the
+    race-check libfa_safe.so). Always recompiles."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, tuple(extra), keep_asm), SOURCES))
-    objs = [o for o, _ in results]
+    jobs = [(src, tuple(extra), None) for src in SOURCES]
+    if safe:
+        jobs += [(src, (*extra, "-DFA_SAFE_SYNC=1"), stem) for src, stem in SAFE_SOURCES.items()]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        results = list(ex.map(lambda j: _compile(j[0], j[1], keep_asm, j[2]), jobs))
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    objs = [o for o, _ in results[:len(SOURCES)]]
+    _link(objs, LIB)
+    if safe:
+        swap = {os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o"): o
+                for (src, _), (o, _) in zip(SAFE_SOURCES.items(), results[len(SOURCES):])}
+        _link([swap.get(o, o) for o in objs], SAFE_LIB)
     return LIB
 
 

@@ -104,8 +104,31 @@
 #define FA_FWD_FAST_PASS 1
 #endif
 
+// Race check (built as a separate library, never the product): 1 waits for
+// every outstanding tile load at each step's end instead of only the ones the
+// next step reads, and adds a workgroup barrier after each LDS read phase
+// (scores and PV). The arithmetic is the same, so its results must equal the
+// pipelined kernel's bit for bit; a tile read before its load landed, or
+// overwritten while another wave still read it, would show as a difference.
+#ifndef FA_SAFE_SYNC
+#define FA_SAFE_SYNC 0
+#endif
+
 namespace fa {
 namespace {
+
+// end of a step: this wave's loads of the tiles the next step reads are in
+// LDS (all of them, in the race-check build), then the workgroup barrier
+template <int INFLIGHT>
+__device__ __forceinline__ void step_sync() {
+  if constexpr (FA_SAFE_SYNC) wait_loads_and_barrier<0>();
+  else wait_loads_and_barrier<INFLIGHT>();
+}
+// end of an LDS read phase: nothing, or (race-check build) a barrier after
+// this wave's LDS reads completed
+__device__ __forceinline__ void phase_sync() {
+  if constexpr (FA_SAFE_SYNC) lds_barrier();
+}
 
 template <int D, int NW, int BN, int S>
 struct FwdCfg {
@@ -561,11 +584,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const bool live = !dead(u, km);
     step_head(u, s_cur, kb0, vb0, u, m_use, alpha, fast);
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
+    phase_sync();
     if constexpr (decltype(fast)::value) bad |= overflow(lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     if (live) pv(vb0, p);
-    wait_loads_and_barrier<C::INFLIGHT>();
+    phase_sync();
+    step_sync<C::INFLIGHT>();
   };
   auto step_hi = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first, auto fast,
@@ -575,11 +600,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const bool prev_live = !first && !dead(u - 1, km_prev);
     step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha, fast);
     if (prev_live) pv(vb0, p_prev);
+    phase_sync();
     const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
+    phase_sync();
     if constexpr (decltype(fast)::value) bad |= overflow(lsum);
     l_run = l_run * alpha + lsum;
     rescale(alpha);
-    wait_loads_and_barrier<C::INFLIGHT>();
+    step_sync<C::INFLIGHT>();
   };
 
   // One pass over the block's key tiles. Safe pass (fast = false): the
@@ -611,7 +638,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     load_k(S - 2, tile_key(S - 2));
     load_k(S - 1, tile_key(S - 1));
-    wait_loads_and_barrier<C::INFLIGHT>();
+    step_sync<C::INFLIGHT>();
     if constexpr (SPARSE) {
       kw0 = list_entry(S - 2);
       kw1 = list_entry(S - 1);

@@ -316,3 +316,29 @@ def probe_heads_inputs(kind, B, H, Hkv, Nq, Nk, d, device, dtype=torch.bfloat16,
     kk = torch.stack(ks).to(dtype).expand(B, Hkv, Nk, d).contiguous()
     vv = torch.stack(vs).to(dtype).expand(B, Hkv, Nk, d).contiguous()
     return qq, kk, vv
+
+
+# Rising scores: the worst case of the forward's fast pass, which fixes each
+# row's reference at its maximum over the first key tile. Q = N(0, 1) + 1 and
+# K = N(0, 1) + ramp(j) with the same ramp on every component of key j, so
+# every row's scores climb by about `slope` (log2 units) per 64 keys; with
+# slope 16 each query block's scores pass its first-tile maximum by more
+# than 2^40 within its first four tiles, so every block fails the fast pass.
+RISING_WORKLOADS = {
+    "rising": dict(name="fwd_causal_bf16_b8h32n16384d128_rising16", B=8, H=32, N=16384, d=128, dtype="bf16",
+                   causal=True, seed=3851, slope=16.0),
+}
+
+
+def make_rising_inputs(cfg, device, shape=None):
+    """Seeded bf16 (q, k, v) of the rising-score recipe above, [B, H, N, d]."""
+    B, H, N, d = shape or (cfg["B"], cfg["H"], cfg["N"], cfg["d"])
+    scale = 1.0 / float(np.sqrt(d))
+    step = cfg["slope"] / (scale * float(np.log2(np.e)) * d)  # per 64 keys, on every component of k
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg["seed"])
+    q = _randn((B, H, N, d), gen, device).add_(1.0).to(torch.bfloat16)
+    ramp = (torch.arange(N, device=device, dtype=torch.float32) / 64 * step).view(1, 1, N, 1)
+    k = _randn((B, H, N, d), gen, device).add_(ramp).to(torch.bfloat16)
+    v = _randn((B, H, N, d), gen, device).to(torch.bfloat16)
+    return q.contiguous(), k.contiguous(), v.contiguous()

@@ -156,9 +156,14 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* 
                    int d, int causal, float scale, hipStream_t stream);
 
 /*
- * Forward, fp32 inputs, fp32 arithmetic, fp32 output; same tiling and online
- * softmax as fa_forward, without bf16 rounding anywhere (for checks that need
- * fp32 accuracy). Same arguments, all tensors fp32.
+ * Forward, fp32 inputs, fp32 arithmetic, fp32 output: the same tiled
+ * computation ("Attention and KV Compression", "Tiling and online softmax":
+ * query blocks, streamed key/value tiles, running maximum, sum and partial
+ * output rescaled as the maximum rises, only O and the per-row statistic
+ * written; the rescale as in "FlashAttention — how 100K-token attention fits
+ * in memory", "Online softmax intuition"), without bf16 rounding anywhere,
+ * for checks that need fp32 accuracy. Same arguments as fa_forward, all
+ * tensors fp32.
  */
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int B, int H, int N, int d, int causal, float scale, hipStream_t stream);

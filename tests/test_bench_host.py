@@ -54,53 +54,90 @@ def test_flop_and_byte_counts_of_the_headline_workload():
     assert bench.algorithmic_fwd_bytes(8, 32, 16384, 128, 8) == (2 * 32 + 2 * 8) * 8 * 16384 * 128 * 2 + 4 * 8 * 32 * 16384
 
 
-def test_counter_record_from_synthetic_run(tmp_path):
+def _ctr_rows_timed(kernel, counters, dur_ns, dispatches=2, start=0):
+    rows, t = [], start
+    for i in range(dispatches):
+        for name, val in counters.items():
+            rows.append({"Dispatch_Id": str(start + i), "Kernel_Name": kernel, "Counter_Name": name,
+                         "Counter_Value": str(val), "Start_Timestamp": str(t), "End_Timestamp": str(t + dur_ns)})
+        t += dur_ns + 10
+    return rows
+
+
+def test_sq_summary_from_synthetic_run(tmp_path):
     # 2 dispatches of 5 ms at 2.0 GHz: 1e7 cycles per XCD, GRBM_GUI_ACTIVE sums 8 XCDs;
     # MFMA busy on 40 % of 1024 SIMDs' cycles; 1 LDS conflict cycle per 100 active
     cycles = 2.0e9 * 5e-3
     counters = {"GRBM_GUI_ACTIVE": 8 * cycles, "SQ_VALU_MFMA_BUSY_CYCLES": 0.4 * cycles * 1024,
                 "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 1000.0, "SQ_INSTS_LDS": 3.0e8,
                 "SQ_INSTS_MFMA": 5.0e8, "SQ_INSTS_VALU": 2.0e9}
-    _write_csv(tmp_path / "ctr.csv", _counter_rows(FWD, counters) + _counter_rows("other_kernel", {
-        "GRBM_GUI_ACTIVE": 1.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1.0}))
-    _write_csv(tmp_path / "trace.csv", _trace_rows(FWD, [5_000_000, 5_000_000]))
-    out = tmp_path / "rec.md"
-    bench.counters_summary(str(tmp_path / "ctr.csv"), str(tmp_path / "trace.csv"), out=str(out))
-    rec = bench.read_record(str(out))
-    assert float(rec["engine_clock_ghz"]) == pytest.approx(2.0, abs=1e-3)
-    assert float(rec["mfma_busy_frac"]) == pytest.approx(0.4, abs=1e-4)
-    assert float(rec["lds_bank_conflict_frac"]) == pytest.approx(0.01, abs=1e-4)
-    assert float(rec["clock_adjusted_peak_tflops"]) == pytest.approx(256 * 4096 * 2.0e9 / 1e12, abs=0.1)
-    assert float(rec["duration_ms"]) == pytest.approx(5.0, abs=1e-3)
+    rows = (_ctr_rows_timed(FWD, counters, 5_000_000)
+            + _ctr_rows_timed("other_kernel", {"GRBM_GUI_ACTIVE": 1.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1.0}, 1000,
+                              start=100))
+    _write_csv(tmp_path / "ctr.csv", rows)
+    ds = bench.read_dispatches(str(tmp_path / "ctr.csv"))
+    assert len(ds) == 4
+    flops = bench.attention_flops(8, 32, 16384, 128, True)
+    rec = bench.sq_summary(ds, "fwd_bf16_kernel", flops)
+    assert rec["dispatches"] == 2
+    assert rec["engine_clock_ghz"] == pytest.approx(2.0, abs=1e-3)
+    assert rec["mfma_busy_frac"] == pytest.approx(0.4, abs=1e-4)
+    assert rec["lds_bank_conflict_frac"] == pytest.approx(0.01, abs=1e-4)
+    assert rec["clock_adjusted_peak_tflops"] == pytest.approx(256 * 4096 * 2.0e9 / 1e12, abs=0.1)
+    assert rec["profiled_duration_ms"] == pytest.approx(5.0, abs=1e-3)
+    assert rec["valu_per_mfma"] == pytest.approx(4.0)
     # 5e8 MFMAs of 32768 FLOPs against 4 N^2 d B H / 2 at the headline shape
-    assert float(rec["mfma_flops_over_algorithmic"]) == pytest.approx(
-        5.0e8 * 32768 / (2 * 16384 ** 2 * 128 * 256), abs=1e-4)
+    assert rec["mfma_flops_over_algorithmic"] == pytest.approx(5.0e8 * 32768 / flops, abs=1e-4)
+    assert bench.sq_summary(ds, "bwd_dq_kernel") is None
 
 
-def test_record_of_other_kernel_sources_is_ignored(tmp_path):
-    out = tmp_path / "rec.md"
-    out.write_text("kernel_source_sha256: " + "0" * 64 + "\nmfma_busy_frac: 0.5\n")
-    assert bench.read_record(str(out)) == {}
-    out.write_text(f"kernel_source_sha256: {bench.fwd_source_hash()}\nmfma_busy_frac: 0.5\n")
-    assert bench.read_record(str(out))["mfma_busy_frac"] == "0.5"
-    assert bench.read_record(str(tmp_path / "missing.md")) == {}
+def test_tcc_summary_scales_by_the_copy_and_checks_decode(tmp_path):
+    # the 1 GiB runtime copy reads 0.5 GiB on the read counter (scale 2) and 1 GiB
+    # on the write counter (scale 1); a bf16 cast reading more must not be taken for it
+    rd, wr = bench.TCC_COUNTERS
+    gib32 = (1 << 30) / 32
+    rows = (_ctr_rows_timed("__amd_rocclr_copyBuffer", {rd: gib32 / 2, wr: gib32}, 1000, 1)
+            + _ctr_rows_timed("void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16_copy_kernel",
+                              {rd: 2 * gib32, wr: gib32}, 1000, 1, start=10)
+            + _ctr_rows_timed(FWD, {rd: 1.0e8, wr: 3.0e7}, 1000, 2, start=20)
+            + _ctr_rows_timed("void fa::(anonymous namespace)::decode_kernel<128, 2, 2, true>(...)",
+                              {rd: 3.0e7, wr: 1.0}, 1000, 2, start=30))
+    _write_csv(tmp_path / "t.csv", rows)
+    t = bench.tcc_summary(bench.read_dispatches(str(tmp_path / "t.csv")), 4.0e9, 2.0e9)
+    assert t["copy_read_scale"] == pytest.approx(2.0) and t["copy_write_scale"] == pytest.approx(1.0)
+    assert t["fwd_read_bytes"] == pytest.approx(32 * 1.0e8 * 2)
+    assert t["fwd_write_bytes"] == pytest.approx(32 * 3.0e7)
+    assert t["fwd_traffic_over_algorithmic"] == pytest.approx((6.4e9 + 9.6e8) / 4.0e9, abs=1e-4)
+    assert t["decode_read_over_known"] == pytest.approx(32 * 3.0e7 * 2 / 2.0e9, abs=1e-4)
 
 
-def test_traffic_record_scales_by_the_copy(tmp_path):
-    # the 1 GiB copy reads 0.5 GiB on FETCH_SIZE (scale 2) and 1 GiB on WRITE_SIZE (scale 1)
-    gib_kib = (1 << 30) / 1024.0
-    fetch = (_counter_rows("void at::native::copy_kernel<float>", {"FETCH_SIZE": gib_kib / 2}, 1)
-             + _counter_rows("void at::native::copy_kernel<float>", {"FETCH_SIZE": 100.0}, 1)
-             + _counter_rows(FWD, {"FETCH_SIZE": 1000.0}, 2))
-    write = (_counter_rows("void at::native::copy_kernel<float>", {"WRITE_SIZE": gib_kib}, 1)
-             + _counter_rows(FWD, {"WRITE_SIZE": 300.0}, 2))
-    _write_csv(tmp_path / "f.csv", fetch)
-    _write_csv(tmp_path / "w.csv", write)
-    out = tmp_path / "traffic.md"
-    bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), out=str(out))
-    assert bench.read_traffic(str(out)) == pytest.approx(1000.0 * 1024 * 2 + 300.0 * 1024 * 1, abs=1.0)
-    out.write_text(out.read_text().replace(bench.fwd_source_hash(), "f" * 64))
-    assert bench.read_traffic(str(out)) is None
+def test_kernel_trace_average_skips_warmup(tmp_path):
+    _write_csv(tmp_path / "k.csv", _trace_rows(FWD, [9_000_000, 9_000_000, 5_000_000, 7_000_000]))
+    ds = bench.read_dispatches(str(tmp_path / "k.csv"))
+    ms, n = bench.kernel_avg_ms(ds, "fwd_bf16_kernel", skip=2)
+    assert n == 2 and ms == pytest.approx(6.0)
+
+
+def test_profile_child_commands():
+    # the program follows `--` directly (no launcher in between); counter passes
+    # stay within one pass's counter budget and never add a system trace
+    for kind in ("trace", "sq", "tcc"):
+        cmd = bench.child_command(kind, "/tmp/x", "rocprofv3", "python3")
+        i = cmd.index("--")
+        assert cmd[i + 1] == "python3" and cmd[i + 2].endswith("bench.py") and cmd[i + 3:] == ["--profile-child", kind]
+        assert not {"-s", "--sys-trace", "-r", "--runtime-trace", "--hip-trace", "--hsa-trace"} & set(cmd)
+        if kind != "trace":
+            pmc = cmd[cmd.index("--pmc") + 1:cmd.index("--output-format")]
+            assert sum(c.startswith("SQ_") for c in pmc) <= 8 and sum(c.startswith("TCC_") for c in pmc) <= 4
+            assert sum(c.startswith("GRBM_") for c in pmc) <= 2
+            assert "--kernel-trace" not in cmd
+
+
+def test_host_cores_respects_affinity_and_omp_cap(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert bench._host_cores() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench._host_cores() == len(os.sched_getaffinity(0))
 
 
 def test_ceiling_record_picks_the_gemm(tmp_path):

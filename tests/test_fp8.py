@@ -170,3 +170,34 @@ def test_fp8_workload_sampled_rows():
         _check_head(_codes(q[b, h]), _codes(k[b, h]), _codes(v[b, h]), qd, kd, vd,
                     o[b, h].float().cpu().numpy()[rows], lse[b, h].cpu().numpy()[rows], scale, True, rows=rows,
                     what=f"head {(b, h)}")
+
+
+def test_fp8_score_error_margin():
+    """delta, the score-error term above, is a measured property of the fp8
+    matrix instruction (its sums are not full fp32), so the test shows the
+    margin it leaves. With Q scaled up the rows are near one-hot: lse is then
+    the row's largest score (plus ln of a sum within 1e-6 of 1), so |lse -
+    lse*| on those rows is that score's error. Its largest ratio to delta is
+    printed and must stay below 1; were the kernel to add an accumulation
+    error of its own, this is where it would show."""
+    _say("fp8 score error margin")
+    B, H, N, d = 1, 4, 600, 128
+    (q, k, v), (qd, kd, vd) = W.make_fp8_inputs(dict(seed=6200), DEV, shape=(B, H, N, d))
+    qd *= 64.0
+    scale = 1 / math.sqrt(d)
+    o, lse = forward_fp8(q, k, v, qd, kd, vd, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    ratios = []
+    for h in range(H):
+        qx, kx = (oracle.e4m3_decode(_codes(c)) * f for c, f in ((q[0, h], qd), (k[0, h], kd)))
+        s = scale * (qx @ kx.T)
+        top2 = np.sort(s, axis=1)[:, -2:]
+        sharp = (top2[:, 1] - top2[:, 0]) > 10.0  # runner-up weight below e^-10
+        _, lse_ref = oracle.forward_fp8(_codes(q[0, h]), _codes(k[0, h]), _codes(v[0, h]), qd, kd, vd, scale, False)
+        delta = EPS_FP8_SUM * scale * (np.abs(qx) @ np.abs(kx).T).max(axis=1)
+        err = np.abs(lse[0, h].cpu().numpy() - lse_ref)
+        ratios.append((err[sharp] / delta[sharp]).max() if sharp.any() else 0.0)
+        assert sharp.sum() >= 50, f"head {h}: only {sharp.sum()} near one-hot rows"
+    margin = max(ratios)
+    print(f"[fp8 margin] largest score error on near one-hot rows / delta = {margin:.3f}", flush=True)
+    assert margin < 1.0
