@@ -564,18 +564,56 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       return false;
     }
   };
-  // (fast pass: flag the wave when a lane's share of a tile's row sum
-  // exceeds 2^40 or is not finite, i.e. when some P may exceed 2^40.) The
-  // test is on the bit pattern: the sum is never negative, so as an unsigned
-  // integer every value above 2^40 (0x53800000), +inf and every NaN of
-  // either sign lies above that of 2^40. This file is built without NaN
-  // semantics, where a float compare may not see a NaN, and the compiler
-  // turns some bit tests back into float compares: the empty asm makes the
-  // bit pattern an opaque integer, so the test stays an integer compare.
+  // (fast pass: true when a lane's share of a tile's row sum exceeds 2^40
+  // or is not finite, i.e. when some P may exceed 2^40.) The test is on the
+  // bit pattern: the sum is never negative, so as an unsigned integer every
+  // value above 2^40 (0x53800000), +inf and every NaN of either sign lies
+  // above that of 2^40. This file is built without NaN semantics, where a
+  // float compare may not see a NaN, and the compiler turns some bit tests
+  // back into float compares: the empty asm makes the bit pattern an opaque
+  // integer, so the test stays an integer compare.
   auto overflow = [&](float lsum) {
     uint32_t bits = __float_as_uint(lsum);
     asm volatile("" : "+v"(bits));
     return __builtin_amdgcn_ballot_w64(bits > 0x53800000u) != 0;
+  };
+  // (fast pass) A tile whose row sums failed the bound but stayed finite,
+  // before its PV: each row's reference moves up by the integer k =
+  // floor(log2(row sum over the tile)) + 1 >= 0, and P, the tile's row sum,
+  // l and acc are scaled by 2^-k. Scaling by a power of two commutes with the
+  // fp32 and bf16 roundings, so the values are exactly those the pass would
+  // have formed with the moved reference, and the tile's largest P is now in
+  // [2^-7, 1). P's bf16 bit patterns (non-negative) are scaled by a
+  // saturating subtraction of k from their exponent fields: a value that
+  // would fall below the normal range becomes 0 or a subnormal, 2^-119 or
+  // more below the tile's largest P.
+  auto rescale_up = [&](bf16x8_t (&p)[BN / 16], float& lsum) __attribute__((always_inline)) {
+    const float rt = halves_sum(lsum);
+    const int k = max((int)(__float_as_uint(rt) >> 23) - 126, 0);
+    m_run += (float)k;
+    lsum = __builtin_amdgcn_ldexpf(lsum, -k);
+    l_run = __builtin_amdgcn_ldexpf(l_run, -k);
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = __builtin_amdgcn_ldexpf(acc[j][e], -k);
+    const uint32_t kk = (uint32_t)k << 7;
+    const u16x2_t sub = {(uint16_t)kk, (uint16_t)kk};
+#pragma unroll
+    for (int i = 0; i < BN / 16; ++i) {
+      u16x2_t* h = (u16x2_t*)&p[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = __builtin_elementwise_sub_sat(h[q], sub);
+    }
+  };
+  // (fast pass) the bookkeeping of a tile whose row sums failed the bound:
+  // rescale in place when every sum is finite, else (a score more than 2^128
+  // above its reference) flag the wave for the checked pass
+  auto on_overflow = [&](bf16x8_t (&p)[BN / 16], float& lsum, bool& bad) __attribute__((always_inline)) {
+    uint32_t bits = __float_as_uint(lsum);
+    asm volatile("" : "+v"(bits));
+    if (__builtin_amdgcn_ballot_w64((bits & 0x7f800000u) == 0x7f800000u)) bad = true;
+    else rescale_up(p, lsum);
   };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p)[BN / 16], auto fast, bool& bad) __attribute__((always_inline)) {
@@ -583,9 +621,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     float m_use, alpha;
     const bool live = !dead(u, km);
     step_head(u, s_cur, kb0, vb0, u, m_use, alpha, fast);
-    const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
+    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
     phase_sync();
-    if constexpr (decltype(fast)::value) bad |= overflow(lsum);
+    if constexpr (decltype(fast)::value) {
+      if (overflow(lsum)) on_overflow(p, lsum, bad);
+    }
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     if (live) pv(vb0, p);
@@ -601,28 +641,32 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha, fast);
     if (prev_live) pv(vb0, p_prev);
     phase_sync();
-    const float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
+    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
     phase_sync();
-    if constexpr (decltype(fast)::value) bad |= overflow(lsum);
+    if constexpr (decltype(fast)::value) {
+      if (overflow(lsum)) on_overflow(p_cur, lsum, bad);
+    }
     l_run = l_run * alpha + lsum;
     rescale(alpha);
     step_sync<C::INFLIGHT>();
   };
 
-  // One pass over the block's key tiles. Safe pass (fast = false): the
+  // One pass over the block's key tiles. Checked pass (fast = false): the
   // lazy reference maximum above, checked on every tile. Fast pass: the
-  // reference of every row is the maximum of its (masked) scores in the
-  // first tile and never moves; no per-tile row maximum is taken. P =
-  // 2^(s2 - m_ref) stays exact for any reference; it only needs bounds so
-  // that P, l and acc stay in range, and the pass checks them through the
-  // row sums it forms anyway: a lane's share of a tile's row sum above 2^40
-  // (or not finite), or an accumulator that is no longer finite at the end,
-  // flags the wave, and the workgroup then reruns the block in the safe
-  // pass. No wide underflow can occur: every row has P = 1 at its first-tile
-  // maximum, so l >= 1. Dense blocks start at key 0, visible to every row;
-  // a block-sparse row that sees no key of its first listed tile has no
-  // finite reference, and the wave is flagged at once. Returns the wave's
-  // flag.
+  // reference of every row starts at the maximum of its (masked) scores in
+  // the first tile, and no per-tile row maximum is taken. P = 2^(s2 - m_ref)
+  // stays exact for any reference; it only needs bounds so that P, l and acc
+  // stay in range, and the row sums the softmax forms anyway check them: a
+  // lane's share of a tile's row sum above 2^40 makes the wave raise its
+  // rows' references by whole powers of two and rescale exactly
+  // (rescale_up), after which the pass goes on. No wide underflow can occur:
+  // every row's largest P so far is at least 2^-7, so l >= 2^-7. The wave is
+  // flagged (returned), and the workgroup runs the block again in the
+  // checked pass, when a row sum is not finite (a score more than 2^128
+  // above its reference), when a row sees no key of the first tile (a
+  // block-sparse list can start with a tile after a row), or when an
+  // accumulator is no longer finite at the end (P <= 2^40 bounds l, but acc
+  // also scales with |V|).
   auto run = [&](auto fast) __attribute__((always_inline)) {
     m_run = -INFINITY;
     l_run = 0.f;
@@ -652,7 +696,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const int k0 = SPARSE ? entry_key(km) : 0;
       if (k0 + BN > N || (CAUSAL && k0 + BN - 1 > row0)) mask(k0, sA);
       m_run = row_max(sA) * c2;
-      // (an ordered compare: no NaN semantics needed)
+      // (a row that sees no key of its first tile has no finite reference:
+      // the checked pass; an ordered compare, no NaN semantics needed)
       bad = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     }
     const int n_steps = (n_tiles + 1) & ~1;

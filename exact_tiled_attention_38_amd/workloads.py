@@ -323,7 +323,8 @@ def probe_heads_inputs(kind, B, H, Hkv, Nq, Nk, d, device, dtype=torch.bfloat16,
 # K = N(0, 1) + ramp(j) with the same ramp on every component of key j, so
 # every row's scores climb by about `slope` (log2 units) per 64 keys; with
 # slope 16 each query block's scores pass its first-tile maximum by more
-# than 2^40 within its first four tiles, so every block fails the fast pass.
+# than 2^40 within its first four tiles, and again every few tiles after
+# each rise of the reference, so the fast pass's bound fails in every block.
 RISING_WORKLOADS = {
     "rising": dict(name="fwd_causal_bf16_b8h32n16384d128_rising16", B=8, H=32, N=16384, d=128, dtype="bf16",
                    causal=True, seed=3851, slope=16.0),
