@@ -478,7 +478,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Step u reads K(u+1) and V(u) (lower) or V(u-1) (upper), and issues
   // V(u+S-2) and K(u+S): V(u+S-2) replaces V(u-2), last read in step u-1;
   // K(u+S) replaces K(u), last read in step u-1 (every wave passed that
-  // step's closing barrier). Loads are issued in the order
+  // step's closing barrier), or for u = 0 by the first tile's scores, which
+  // a barrier of their own closes. Loads are issued in the order
   // K0 V0 K1 V1 ... K(S-3) V(S-3) K(S-2) K(S-1), then V(u+S-2) K(u+S) per
   // step; at the end of step u the next step needs V(u+1) (and the older
   // K(u+2)), after which 2S-5 tiles' loads were issued, so each wave waits
@@ -690,6 +691,10 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       km = list_entry(0);
     }
     qk(k_addr(0), sA);
+    // step 0 loads K(S) into slot 0, which every wave has just read: wait
+    // until they all have (otherwise only the load's latency keeps a slow
+    // wave from reading tile S's keys in place of tile 0's)
+    lds_barrier();
     bool bad = false;
     if constexpr (decltype(fast)::value) {
       // (the first tile's key: the mask step_head(0) applies again)

@@ -326,6 +326,9 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
 #pragma unroll
   for (int i = 0; i < BN / 64; ++i) pA[i] = pB[i] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   qk(k_base(0), sA);
+  // step 0 loads K(S) into slot 0, which every wave has just read: wait
+  // until they all have
+  lds_barrier();
   if constexpr (FA_FP8_SUMCHECK) {
     // key 0 is visible to every row: the first tile's masked maximum is a
     // finite initial reference (step_head(0) applies the same mask again)

@@ -253,3 +253,22 @@ def test_outputs_write_nothing_outside_their_bounds():
     assert torch.all(obuf[:pad] == -7.0) and torch.all(obuf[pad + n_o:] == -7.0)
     assert torch.all(lbuf[:pad] == -7.0) and torch.all(lbuf[pad + n_l:] == -7.0)
     assert torch.all(torch.isfinite(o.float())) and torch.all(torch.isfinite(lse))
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(8, 32, 2048, False), (4, 16, 4099, True)])
+def test_bf16_many_units_per_workgroup_deterministic(B, H, N, causal):
+    """Shapes with more (head, query block) units than compute units, so each
+    workgroup runs several units in turn and its waves reuse the LDS ring
+    across them: repeated launches must agree bit for bit (a wave reading a
+    ring slot that another wave's next load already overwrote would not),
+    and one head is checked against the oracle."""
+    _say("many units", B, H, N, causal)
+    cfg = dict(dtype="bf16", seed=31 + N, q_mult=4.0)
+    q, k, v = W.make_inputs(cfg, DEV, shape=(B, H, N, 128))
+    scale = 1 / math.sqrt(128)
+    first = forward(q, k, v, causal=causal, scale=scale)
+    for _ in range(6):
+        again = forward(q, k, v, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    _check_heads(q, k, v, first[0], first[1], scale, causal, [(B - 1, H - 1)])
