@@ -76,10 +76,14 @@ SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_A
                "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
 TCC_COUNTERS = ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
 CHILD_TIMEOUT_S = 240
+# minimum warm-up wall time before timing the shorter workloads (the headline
+# keeps exactly --warmup steps)
+WARM_MS = 150.0
 # kernels named in the records (substring of the demangled name -> short name)
 KERNELS = {"fwd_bf16_kernel": "fwd_bf16_kernel", "bwd_dkdv_kernel": "bwd_dkdv_kernel",
            "bwd_dq_kernel": "bwd_dq_kernel", "bwd_preprocess_kernel": "bwd_preprocess_kernel",
-           "decode_kernel": "decode_kernel", "merge_kernel": "merge_kernel", "merge_wide_kernel": "merge_wide_kernel"}
+           "decode_kernel": "decode_kernel", "merge_kernel": "merge_kernel", "merge_wide_kernel": "merge_wide_kernel",
+           "fwd_fp8_kernel": "fwd_fp8_kernel", "fwd_f32_kernel": "fwd_f32_kernel"}
 
 
 def log(*a):
@@ -126,6 +130,9 @@ def parse(argv=None):
                     help="keep the rocprofv3 output and write the summary records into DIR")
     ap.add_argument("--profile-child", choices=["trace", "sq", "tcc"], help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "WORKLOAD"),
+                    help="no GPU work: turn the run_kernel_stats.csv of one rocprofv3 --kernel-trace --stats run "
+                         "of `bench.py --workload WORKLOAD` into a kernel-statistics record (stdout)")
     ap.add_argument("--ceiling-summary", nargs=2, metavar=("COUNTER_CSV", "TRACE_CSV"),
                     help="no GPU work: turn one rocprofv3 --pmc --kernel-trace run of "
                          "`bench.py --workload gemm_ceiling` into the GEMM ceiling record under profiles/")
@@ -141,7 +148,8 @@ def short_name(name):
             return short
     if "copyBuffer" in name:  # the runtime's device-to-device copy (torch's same-dtype copy_)
         return "device_copy"
-    return name.split("(")[0][:60]
+    name = name[5:] if name.startswith("void ") else name
+    return name.replace("(anonymous namespace)::", "").split("(")[0][:60]
 
 
 def read_dispatches(path):
@@ -401,15 +409,24 @@ def write_profile_records(outdir, paths, prof, launch_avg_ms):
 # ---------------------------------------------------------------- timing
 
 
-def time_launches(fn, steps, warmup, stream, between=None):
-    """Run fn `warmup` times, then `steps` timed times, each bracketed by HIP
-    events on `stream`; `between` (untimed) runs before each timed launch.
-    Returns (ms of the whole timed region, per-launch ms list)."""
+def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0):
+    """Run fn `warmup` times (and, with warm_ms, on until that much wall time
+    has passed: a sub-millisecond kernel needs ~0.1 s of work before the
+    clocks settle), then `steps` timed times, each bracketed by HIP events on
+    `stream`; `between` (untimed) runs before each timed launch. Returns (ms
+    of the whole timed region, per-launch ms list)."""
     import torch
 
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(5):
+            if between is not None:
+                between()
+            fn()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -508,6 +525,68 @@ def ceiling_summary(counter_csv, trace_csv, out=None):
     print("\n".join(lines))
 
 
+def workload_figures(workload):
+    """(kernel short name, description, algorithmic FLOPs or None, algorithmic bytes or None)
+    of one launch of a bench workload's main kernel."""
+    from exact_tiled_attention_38_amd import workloads as W
+
+    if workload.startswith("decode"):
+        c = W.DECODE_WORKLOADS[workload]
+        return ("decode_kernel", f"decode, B={c['B']} H={c['H']} Hkv={c['Hkv']} Nq={c['Nq']} Nk={c['Nk']} "
+                f"d={c['d']}; the whole call adds a merge kernel", None, decode_bytes(c))
+    if workload == "sparse":
+        c = W.SPARSE_WORKLOADS["sparse"]
+        rp, cols = W.sparse_selection(c["B"], c["H"], c["N"], c["seed"], c["keep"])
+        pairs = W.sparse_visible_pairs(c["N"], rp, cols, c["B"] * c["H"], c["causal"])
+        return ("fwd_bf16_kernel", f"block-sparse forward, causal B={c['B']} H={c['H']} N={c['N']} d={c['d']}, "
+                f"{cols.shape[0]} listed 256x64 blocks, {pairs:.4g} kept pairs", 4.0 * c["d"] * pairs, None)
+    if workload == "fp8":
+        c = W.FP8_WORKLOADS["fp8"]
+        return ("fwd_fp8_kernel", f"fp8 (e4m3) forward, causal B={c['B']} H={c['H']} N={c['N']} d={c['d']}",
+                attention_flops(c["B"], c["H"], c["N"], c["d"], True), None)
+    if workload in ("gqa", "mqa"):
+        c = W.GQA_WORKLOADS[workload]
+        return ("fwd_bf16_kernel", f"forward with shared heads, causal B={c['B']} H={c['H']} Hkv={c['Hkv']} "
+                f"N={c['N']} d={c['d']}", attention_flops(c["B"], c["H"], c["N"], c["d"], True),
+                algorithmic_fwd_bytes(c["B"], c["H"], c["N"], c["d"], c["Hkv"]))
+    raise ValueError(workload)
+
+
+def stats_summary(stats_csv, workload):
+    """Kernel-statistics record of one rocprofv3 --kernel-trace --stats run of
+    `bench.py --workload WORKLOAD` (returned as text)."""
+    import csv
+
+    kernel, desc, flops, nbytes = workload_figures(workload)
+    fp8 = workload == "fp8"
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = [f"Kernel statistics (rocprofv3 --kernel-trace --stats) of bench.py's {workload} workload on one MI355X:",
+           desc + ".",
+           "Commands (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
+           f"  rocprofv3 --kernel-trace --stats --output-format csv -d <out>/{workload} -o run -- \\",
+           f"      python3 bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline",
+           f"  python bench.py --stats-summary <out>/{workload}/run_kernel_stats.csv {workload}",
+           "",
+           f"{'kernel':62s} {'calls':>6s} {'average_ns':>12s} {'min_ns':>12s} {'max_ns':>12s}"]
+    avg = None
+    for r in rows:
+        name = short_name(r["Name"])
+        if name == kernel and avg is None:
+            avg = float(r["AverageNs"]) * 1e-9
+        out.append(f"{name[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']):12.0f} "
+                   f"{float(r['MinNs']):12.0f} {float(r['MaxNs']):12.0f}")
+    out.append("")
+    if avg and flops:
+        peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+        tf = flops / avg / 1e12
+        out.append(f"{kernel}: {flops:.4g} algorithmic FLOPs / {avg * 1e3:.4f} ms = {tf:.1f} TFLOP/s "
+                   f"({tf / peak:.4f} of the {peak} {'fp8' if fp8 else 'bf16'} peak)")
+    if avg and nbytes:
+        out.append(f"{kernel}: {nbytes:.4g} algorithmic bytes / {avg * 1e3:.4f} ms = {nbytes / avg / 1e9:.1f} GB/s "
+                   f"({nbytes / avg / 1e9 / PEAK_HBM_GBS:.4f} of 8 TB/s)")
+    return "\n".join(out) + "\n"
+
+
 def read_ceiling(path=None):
     try:
         rec = {}
@@ -599,11 +678,21 @@ def bench_decode(a, cfg):
     ws = torch.empty(fa.decode_workspace_bytes(B, H, Hkv, Nq, Nk, d), dtype=torch.uint8, device=dev)
     scale = 1.0 / d ** 0.5
     step = lambda: fa.decode(q, k, v, causal=cfg["causal"], scale=scale, workspace=ws, out=o, lse=lse)
-    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream, warm_ms=WARM_MS)
     ms = total_ms / a.steps
     nbytes = decode_bytes(cfg)
-    launch_avg = sum(per) / len(per)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # A call is ~0.1 ms, about what the Python binding takes to issue it, so
+    # eager timing includes idle time between calls. Serving loops replay
+    # captured HIP graphs instead: time CALLS calls captured in one graph
+    # (the same kernels and arguments), which measures the kernels' own time.
+    calls = 10
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            step()
+    replay_total, _ = time_launches(graph.replay, max(2, a.steps // 2), 2, stream, warm_ms=WARM_MS)
+    launch_avg = replay_total / max(2, a.steps // 2) / calls
     achieved = nbytes / (launch_avg * 1e-3) / 1e9
     return {
         "metric": "attention decode: algorithmic HBM bytes per second (K and V read once)",
@@ -621,8 +710,10 @@ def bench_decode(a, cfg):
         "config": {"workload": f"bf16 decode, B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d}"
                                + (" causal" if cfg["causal"] else ""),
                    "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "causal": bool(cfg["causal"])},
+        "eager_ms_per_call": round(ms, 5),
+        "graph_ms_per_call": round(launch_avg, 5),
         "roofline": {
-            "kernel": "decode_kernel + merge_kernel (one fa_decode call)",
+            "kernel": "decode_kernel + merge_kernel (one fa_decode call, from HIP-graph replays of 10 calls)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
@@ -653,7 +744,7 @@ def bench_sparse(a, cfg):
     cols_t = torch.tensor(cols, dtype=torch.int32, device=dev)
     scale = 1.0 / d ** 0.5
     step = lambda: fa.forward_block_sparse(q, k, v, row_ptr, cols_t, causal=cfg["causal"], scale=scale)
-    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream, warm_ms=WARM_MS)
     ms = total_ms / a.steps
     flops = 4.0 * d * pairs
     launch_avg = sum(per) / len(per)
@@ -703,7 +794,7 @@ def bench_fp8(a, cfg):
     (q, k, v), (qd, kd, vd) = W.make_fp8_inputs(cfg, dev)
     scale = 1.0 / d ** 0.5
     step = lambda: fa.forward_fp8(q, k, v, qd, kd, vd, causal=cfg["causal"], scale=scale)
-    total_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream, warm_ms=WARM_MS)
     ms = total_ms / a.steps
     flops = attention_flops(B, H, N, d, cfg["causal"])
     launch_avg = sum(per) / len(per)
@@ -762,9 +853,9 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fl = attention_flops(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"])
     fwd = lambda: fa.forward(q, k, v, causal=cfg["causal"], scale=cfg["scale"], out=o, lse=lse)
-    _, warm = time_launches(fwd, steps, warmup, stream)
+    _, warm = time_launches(fwd, steps, warmup, stream, warm_ms=WARM_MS)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    _, cold = time_launches(fwd, steps, warmup, stream, between=lambda: flush.fill_(1))
+    _, cold = time_launches(fwd, steps, warmup, stream, between=lambda: flush.fill_(1), warm_ms=WARM_MS)
     out["config2"] = {"workload": "non-causal bf16 forward, B=8 H=32 N=2048 d=128, Q x4",
                       "flops": fl, "warm": _fwd_entry(warm, fl), "cold": _fwd_entry(cold, fl)}
     del q, k, v, o, lse, flush
@@ -775,7 +866,7 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fl = attention_flops(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"])
     _, per = time_launches(lambda: fa.forward(q, k, v, causal=True, scale=cfg["scale"], out=o, lse=lse),
-                           steps, warmup, stream)
+                           steps, warmup, stream, warm_ms=WARM_MS)
     out["config4"] = {"workload": "causal bf16 forward, B=1 H=8 N=100000 d=128", "flops": fl,
                       **_fwd_entry(per, fl)}
     del q, k, v, o, lse
@@ -787,9 +878,9 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
     ws = torch.empty(fa.backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     fl = 2.5 * attention_flops(B, H, N, d, True)
     bwd = lambda: fa.backward(q, k, v, o, do, lse, causal=True, scale=cfg["scale"], workspace=ws)
-    _, warm = time_launches(bwd, steps, warmup, stream)
+    _, warm = time_launches(bwd, steps, warmup, stream, warm_ms=WARM_MS)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    _, cold = time_launches(bwd, steps, warmup, stream, between=lambda: flush.fill_(1))
+    _, cold = time_launches(bwd, steps, warmup, stream, between=lambda: flush.fill_(1), warm_ms=WARM_MS)
     out["config5_backward"] = {"workload": "backward of causal bf16 attention, B=4 H=16 N=4096 d=128 "
                                            "(dq, dk, dv; 3 kernels)",
                                "flops": fl, "warm": _fwd_entry(warm, fl), "cold": _fwd_entry(cold, fl)}
@@ -800,7 +891,8 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     fl = attention_flops(cfg["B"], cfg["H"], cfg["N"], cfg["d"], True)
-    _, per = time_launches(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse), steps, warmup, stream)
+    _, per = time_launches(lambda: fa.forward(q, k, v, causal=True, out=o, lse=lse), steps, warmup, stream,
+                           warm_ms=WARM_MS)
     e = _fwd_entry(per, fl)
     out["worst_case"] = {
         "workload": f"causal bf16 forward, B=8 H=32 N=16384 d=128, scores rising by {cfg['slope']:g} (log2) "
@@ -816,6 +908,9 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
 
 def main():
     a = parse()
+    if a.stats_summary:
+        print(stats_summary(*a.stats_summary), end="")
+        return
     if a.ceiling_summary:
         ceiling_summary(*a.ceiling_summary)
         return

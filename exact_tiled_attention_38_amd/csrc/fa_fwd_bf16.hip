@@ -274,6 +274,18 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto load_k = [&](int t, int k0) { load_tile(Kh, t, 0, dk_off, k0); };
   auto load_v = [&](int t, int k0) { load_tile(Vh, t, S, dv_off, k0); };
+  // The same loads one wave-wide DMA at a time, so a step can spread them
+  // over its matrix instructions: part j < NDMA is V tile vt's load j, the
+  // rest K tile kt's. Rows are always clamped (a no-op below the tail).
+  auto load_part = [&](int j, int vt, int vk0, int kt, int kk0) __attribute__((always_inline)) {
+    const bool is_v = j < C::NDMA;
+    const int i = is_v ? j : j - C::NDMA;
+    const int k0 = is_v ? vk0 : kk0;
+    const int slot = (is_v ? S : 0) + ((is_v ? vt : kt) & (S - 1));
+    const char* base = (const char*)((is_v ? Vh : Kh) + (size_t)k0 * D);
+    FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024 + i * 1024;
+    dma16(base, clamp_row(is_v ? dv_off[i] : dk_off[i], N - 1 - k0), dst);
+  };
 
   // ---- Q^T operand: lane holds Q[qrow][16c + 8h .. +7]
   bf16x8_t qf[D / 16];
@@ -385,11 +397,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Scores of the next tile (K at kb0) on the matrix cores, interleaved
   // slice by slice with the softmax of the current tile on the vector unit
   // (exponentials, row sum, bf16 rounding of P). Returns the row sum.
+  // kpre: the first LA_K K operands, already read (or null: read here).
+  // vout: if not null, the last slices also read the first LA_V V operands
+  // of the PV product at vb_next that follows, so it need not wait for LDS.
   auto qk_softmax = [&](int kb0, float m_use, float alpha, const f32x16_t (&s_cur)[BN / 32],
-                        f32x16_t (&s_nxt)[BN / 32], bf16x8_t (&p)[BN / 16]) __attribute__((always_inline)) {
+                        f32x16_t (&s_nxt)[BN / 32], bf16x8_t (&p)[BN / 16], const bf16x8_t* kpre,
+                        int vb_next, bf16x8_t* vout) __attribute__((always_inline)) {
     bf16x8_t kr[KQ];
 #pragma unroll
-    for (int i = 0; i < LA_K; ++i) kr[i] = kread(kb0, i);
+    for (int i = 0; i < LA_K; ++i) kr[i] = kpre ? kpre[i] : kread(kb0, i);
     float lsum = 0.f;
     // The two waves of a SIMD contend for its issue port and matrix core, and
     // a wave issues in order: while this one interleaves score MFMAs with
@@ -399,16 +415,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // (2-3 % on the causal N = 16384 forward; results unchanged).
     if constexpr (FA_FWD_PRIO_QK > 0) __builtin_amdgcn_s_setprio(FA_FWD_PRIO_QK);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < KQ; ++i) {
-      if (i + LA_K < KQ) kr[i + LA_K] = kread(kb0, i + LA_K);
-      const int c = i / (BN / 32), kb = i % (BN / 32);
-      if (c == 0) {
-        const f32x16_t z = {};
-        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], z);
-      } else {
-        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], s_nxt[kb]);
-      }
+    // softmax values of slice i (exponentials, row sum, bf16 rounding)
+    auto softmax_slice = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < VPS; e += 2) {
         const int f = i * VPS + e;  // flat index of the value within the lane's BN/2
@@ -419,6 +427,19 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         p[f >> 3][f & 7] = pb[0];
         p[f >> 3][(f + 1) & 7] = pb[1];
       }
+    };
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      if (i + LA_K < KQ) kr[i + LA_K] = kread(kb0, i + LA_K);
+      if (vout && i >= KQ - LA_V) vout[i - (KQ - LA_V)] = vread(vb_next, i - (KQ - LA_V));
+      const int c = i / (BN / 32), kb = i % (BN / 32);
+      if (c == 0) {
+        const f32x16_t z = {};
+        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], z);
+      } else {
+        s_nxt[kb] = mfma_32x32x16(kr[i], qf[c], s_nxt[kb]);
+      }
+      softmax_slice(i);
       if constexpr (FA_FWD_RESCALE_IN_SLICES) {
         constexpr int per = D / 2 / KQ;  // accumulator values rescaled per slice
 #pragma unroll
@@ -450,19 +471,34 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // acc += P V for the V tile at vb0
-  auto pv = [&](int vb0, const bf16x8_t (&p)[BN / 16]) __attribute__((always_inline)) {
+  // acc += P V for the V tile at vb0, with the step's 2 NDMA tile loads
+  // (ld: V tile, its first key, K tile, its first key; none if ld[0] < 0)
+  // issued one every KP / (2 NDMA) matrix instructions
+  constexpr int LD_EVERY = KP / (2 * C::NDMA);
+  static_assert(LD_EVERY >= 1 && KP % (2 * C::NDMA) == 0, "load spread");
+  // (vpre: the first LA_V V operands, already read by the caller, or null;
+  // kout: if not null, the last slices read the first LA_K K operands of the
+  // scores at kb_next that follow)
+  auto pv = [&](int vb0, const bf16x8_t (&p)[BN / 16], const int (&ld)[4], const bf16x8_t* vpre,
+                int kb_next, bf16x8_t* kout) __attribute__((always_inline)) {
     bf16x8_t vr[KP];
 #pragma unroll
-    for (int k = 0; k < LA_V; ++k) vr[k] = vread(vb0, k);
+    for (int k = 0; k < LA_V; ++k) vr[k] = vpre ? vpre[k] : vread(vb0, k);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
       if (k + LA_V < KP) vr[k + LA_V] = vread(vb0, k + LA_V);
+      if (kout && k >= KP - LA_K) kout[k - (KP - LA_K)] = kread(kb_next, k - (KP - LA_K));
+      if (k % LD_EVERY == LD_EVERY / 2 && ld[0] >= 0) load_part(k / LD_EVERY, ld[0], ld[1], ld[2], ld[3]);
       const int j = k / (BN / 16), kc = k % (BN / 16);
       acc[j] = mfma_32x32x16(vr[k], p[kc], acc[j]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // the step's loads when it has no PV product to carry them
+  auto loads_only = [&](const int (&ld)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2 * C::NDMA; ++j) load_part(j, ld[0], ld[1], ld[2], ld[3]);
   };
 
   // ---- pipeline over key tiles. K(t) and V(t) live in ring slot t % S.
@@ -481,10 +517,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // step's closing barrier), or for u = 0 by the first tile's scores, which
   // a barrier of their own closes. Loads are issued in the order
   // K0 V0 K1 V1 ... K(S-3) V(S-3) K(S-2) K(S-1), then V(u+S-2) K(u+S) per
-  // step; at the end of step u the next step needs V(u+1) (and the older
-  // K(u+2)), after which 2S-5 tiles' loads were issued, so each wave waits
-  // until at most that many DMAs are outstanding, then the barrier publishes
-  // the tiles to all waves.
+  // step, spread over the step's PV product; at the end of step u the next
+  // step needs V(u+1) (and the older K(u+2)), after which 2S-5 tiles' loads
+  // were issued, so each wave waits until at most that many DMAs are
+  // outstanding, then the barrier publishes the tiles to all waves.
+  // Operands are read ahead across phase boundaries where their tiles are
+  // already published: the lower half reads its first V operands in the
+  // last score slices, the upper half its first K operands in the last PV
+  // slices and its next step's first V operands (V(u), published since
+  // step u began) between its wait and the barrier.
   // Block-sparse: the first keys of the tiles a step loads (u+S-2 for V, u+S
   // for K) and masks (u) come from the list; they are read one step ahead
   // (scalar loads) and passed along, so no step waits for its own list reads.
@@ -492,6 +533,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int kw0 = 0, kw1 = 0, kw2 = 0, km = 0, km_prev = 0;
   f32x16_t sA[BN / 32], sB[BN / 32];
   bf16x8_t pA[BN / 16], pB[BN / 16];
+  bf16x8_t vpre[LA_V];  // (upper half) V operands read ahead across the barrier
 
 
   // Every wave runs every step of the workgroup's key range, with no
@@ -508,11 +550,16 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // an empty asm statement so the per-chunk XORs are formed here rather than
   // kept live across the loop), row max and alpha.
   auto step_head = [&](int u, f32x16_t (&s_cur)[BN / 32], int& kb0, int& vb0, int v_tile,
-                  float& m_use, float& alpha, auto fast) __attribute__((always_inline)) {
+                  float& m_use, float& alpha, int (&ld)[4], auto fast) __attribute__((always_inline)) {
+    // the step's loads (V tile u+S-2, K tile u+S and their first keys) are
+    // issued during its PV product (load_part), not here: right after the
+    // barrier every wave would queue its loads at once
+    ld[0] = u + S - 2;
+    ld[2] = u + S;
     if constexpr (SPARSE) {
       const int nk = list_entry(u + S + 1), nm = list_entry(u + 1);  // for the next step
-      load_v(u + S - 2, entry_key(kw0));
-      load_k(u + S, entry_key(kw2));
+      ld[1] = entry_key(kw0);
+      ld[3] = entry_key(kw2);
       // the even-count padding step (u = n_tiles) is masked entirely
       const int k0 = u < n_tiles ? entry_key(km) : N;
       if (k0 >= N || (CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
@@ -522,8 +569,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       km_prev = km;
       km = nm;
     } else {
-      load_v(u + S - 2, tile_key(u + S - 2));
-      load_k(u + S, tile_key(u + S));
+      ld[1] = tile_key(u + S - 2);
+      ld[3] = tile_key(u + S);
       const int k0 = u * BN;
       if ((CAUSAL && k0 + BN - 1 > row0) || k0 + BN > N) mask(k0, s_cur);
     }
@@ -618,38 +665,59 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto step_lo = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p)[BN / 16], auto fast, bool& bad) __attribute__((always_inline)) {
-    int kb0, vb0;
+    int kb0, vb0, ld[4];
     float m_use, alpha;
     const bool live = !dead(u, km);
-    step_head(u, s_cur, kb0, vb0, u, m_use, alpha, fast);
-    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p);
+    step_head(u, s_cur, kb0, vb0, u, m_use, alpha, ld, fast);
+    bf16x8_t vnext[LA_V];
+    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p, nullptr, vb0, vnext);
     phase_sync();
     if constexpr (decltype(fast)::value) {
       if (overflow(lsum)) on_overflow(p, lsum, bad);
     }
     l_run = l_run * alpha + lsum;
     rescale(alpha);
-    if (live) pv(vb0, p);
+    if (live) pv(vb0, p, ld, vnext, 0, nullptr);
+    else loads_only(ld);
     phase_sync();
     step_sync<C::INFLIGHT>();
+  };
+  // End of an upper-half step u: like step_sync, but between the wait and
+  // the barrier the wave reads the first V operands of step u+1's PV, V(u),
+  // so they arrive while it waits for the other waves. V(u) landed before
+  // step u began, and its slot is next refilled in step u+2.
+  auto step_sync_vpre = [&](int u, bf16x8_t (&vpre)[LA_V]) __attribute__((always_inline)) {
+    if constexpr (FA_SAFE_SYNC) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(C::INFLIGHT) : "memory");
+    const int vb_next = v_addr(u & (S - 1));
+#pragma unroll
+    for (int k = 0; k < LA_V; ++k) vpre[k] = vread(vb_next, k);
+    asm volatile("s_barrier" ::: "memory");
   };
   auto step_hi = [&](int u, f32x16_t (&s_cur)[BN / 32], f32x16_t (&s_nxt)[BN / 32],
                      bf16x8_t (&p_cur)[BN / 16], const bf16x8_t (&p_prev)[BN / 16], bool first, auto fast,
                      bool& bad) __attribute__((always_inline)) {
-    int kb0, vb0;
+    int kb0, vb0, ld[4];
     float m_use, alpha;
     const bool prev_live = !first && !dead(u - 1, km_prev);
-    step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha, fast);
-    if (prev_live) pv(vb0, p_prev);
+    step_head(u, s_cur, kb0, vb0, u - 1, m_use, alpha, ld, fast);
+    bf16x8_t knext[LA_K];
+    if (prev_live) {
+      pv(vb0, p_prev, ld, vpre, kb0, knext);
+    } else {
+      loads_only(ld);
+#pragma unroll
+      for (int i = 0; i < LA_K; ++i) knext[i] = kread(kb0, i);
+    }
     phase_sync();
-    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur);
+    float lsum = qk_softmax(kb0, m_use, alpha, s_cur, s_nxt, p_cur, knext, 0, nullptr);
     phase_sync();
     if constexpr (decltype(fast)::value) {
       if (overflow(lsum)) on_overflow(p_cur, lsum, bad);
     }
     l_run = l_run * alpha + lsum;
     rescale(alpha);
-    step_sync<C::INFLIGHT>();
+    step_sync_vpre(u, vpre);
   };
 
   // One pass over the block's key tiles. Checked pass (fast = false): the
@@ -719,7 +787,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
       step_hi(n_steps - 1, sB, sA, pB, pA, false, fast, bad);
       // (the list entries have moved on by one step: km_prev is tile n_steps - 1's)
-      if (!dead(n_steps - 1, km_prev)) pv(v_addr((n_steps - 1) & (S - 1)), pB);
+      const int no_loads[4] = {-1, 0, 0, 0};
+      if (!dead(n_steps - 1, km_prev)) pv(v_addr((n_steps - 1) & (S - 1)), pB, no_loads, vpre, 0, nullptr);
     }
     // no load may still be writing this workgroup's LDS when the pass ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
