@@ -29,7 +29,8 @@
 //     the forward: each lane owns one query row and 16 keys of each 32.
 //   * The waves of a workgroup take interleaved 32-key tiles of the split.
 //     Each wave has its own ring of SLOTS K and V tiles in LDS, filled by
-//     direct-to-LDS 16-byte loads and refilled as soon as a tile is read, so
+//     non-temporal direct-to-LDS 16-byte loads (each byte is read once, so
+//     the caches need not keep it) and refilled as soon as a tile is read, so
 //     up to SLOTS - 1 tiles per wave are in flight while it computes; the
 //     waves never wait for each other inside the loop.
 //   * The mask (keys past the split or past a query's position) is applied
@@ -69,11 +70,13 @@ void* g_scratch_ptr[kMaxDevices] = {};
 #ifndef FA_DEC_SLOTS128
 #define FA_DEC_SLOTS128 2
 #endif
-// Fewest workgroups a launch is split into: two per compute unit (two fit
-// in its LDS, and each adds its loads in flight); 256, 384 and 768 were 2-3 %
-// slower on the 100K-token and shared-head caches
+// Fewest workgroups a launch is split into: one per compute unit. With the
+// non-temporal loads one workgroup's two waves keep enough bytes in flight;
+// 320 or 384 leave some compute units with two workgroups and a tail, and
+// 512 (two per unit) was 5-6 % slower on the 100K-token and shared-head
+// caches (equal on the 16K one)
 #ifndef FA_DEC_MIN_WG
-#define FA_DEC_MIN_WG 512
+#define FA_DEC_MIN_WG 256
 #endif
 #ifndef FA_DEC_SLOTS64
 #define FA_DEC_SLOTS64 4
@@ -174,8 +177,9 @@ decode_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = 0; i < C::NDMA; ++i) {
       const int row = i * C::RPW + dma_row;
       const uint32_t kr = (uint32_t)min(k0 + row, span) * C::ROWB;
-      dma16(Kb, kr + 16 * (dma_chunk ^ kswz<D>(row)), kd + i * 1024);
-      dma16(Vb, kr + 16 * (dma_chunk ^ vswz<D>(row)), vd + i * 1024);
+      // (each K/V byte is read once: non-temporal)
+      dma16_nt(Kb, kr + 16 * (dma_chunk ^ kswz<D>(row)), kd + i * 1024);
+      dma16_nt(Vb, kr + 16 * (dma_chunk ^ vswz<D>(row)), vd + i * 1024);
     }
   };
 
