@@ -185,6 +185,25 @@ def test_gradients_deterministic_and_workspace_contents_irrelevant():
     _check(q, k, v, do, dq1, dk1, dv1, True, 1 / math.sqrt(d), [(0, 0), (1, 2)])
 
 
+@pytest.mark.parametrize("kv_heads", [16, 4])
+def test_gradients_bitwise_repeatable_over_many_workgroups(kv_heads):
+    """The dK/dV kernel hands P from one wave to its partner through LDS and
+    streams query tiles through a shared ring: at config 5's shape (B4 H16
+    N4096; 512 workgroups in flight at once, in whatever interleaving the
+    device picks) repeated runs must agree bit for bit, with shared K/V
+    heads too."""
+    _say("bwd repeatability", kv_heads)
+    cfg = W.config(5)
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    q, k, v, do = W.make_inputs(cfg, DEV, with_do=True, kv_heads=kv_heads)
+    o, lse = forward(q, k, v, causal=True)
+    first = backward(q, k, v, o, do, lse, causal=True)
+    for rep in range(6):
+        again = backward(q, k, v, o, do, lse, causal=True)
+        for name, a_, b_ in zip(("dq", "dk", "dv"), first, again):
+            assert torch.equal(a_, b_), f"{name} differs in repeat {rep}"
+
+
 def test_backward_outputs_write_nothing_outside_their_bounds():
     _say("bwd guard bands")
     B, H, N, d = 1, 2, 301, 128
