@@ -313,3 +313,28 @@ def test_decode_noalloc_error_paths(L):
     assert call([A + 8] + [A] * 4) == CODES["FA_ERR_ALIGN"]
     assert call([A] * 5, B=8, H=32, Hkv=32, Nq=4, Nk=200000) == CODES["FA_ERR_SCRATCH"]
     assert "static scratch" in _lib.status_string(CODES["FA_ERR_SCRATCH"])
+
+
+def _library_sources():
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    assert "fa_api.hip" in names and "fa_fwd_bf16.hip" in names
+    out = {}
+    for f in names:
+        text = open(os.path.join(CSRC, f)).read()
+        # code only: comments may name what the code deliberately avoids
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        out[f] = re.sub(r"//[^\n]*", "", text)
+    return out
+
+
+def test_library_source_never_allocates_frees_or_synchronizes():
+    """The boundary promises that the library allocates, frees and waits for
+    nothing (all work is enqueued on the caller's stream, every buffer is the
+    caller's or static): the sources call no allocator, free, memset or
+    synchronisation routine of the runtime. (A memset node recorded in a
+    captured graph would also be a hazard for graph replays.)"""
+    banned = re.compile(r"\b(hipMalloc\w*|hipExtMalloc\w*|hipHostMalloc|hipMallocAsync|hipFree\w*|"
+                        r"hipMemset\w*|hipDeviceSynchronize|hipStreamSynchronize|hipEventSynchronize|"
+                        r"hipMemcpy\w*|hipHostRegister)\b")
+    found = {f: sorted(set(banned.findall(t))) for f, t in _library_sources().items()}
+    assert not any(found.values()), {f: v for f, v in found.items() if v}
