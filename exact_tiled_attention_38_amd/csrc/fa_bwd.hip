@@ -107,22 +107,23 @@ bwd_preprocess_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict
 // vector work, the other feeds the matrix core, and each wave reads half
 // the LDS bytes per tile. (One wave per SIMD doing all four products in 376
 // registers was LDS-issue bound at 0.50 MFMA busy; this split is 2.6-3.7 %
-// faster over the whole backward. dS uses P rounded to bf16, as passed.) The query tiles (and, with
-// shared key/value heads, the tiles of every head of the group in turn) form
-// one stream; step s loads tile s + 1 into a 3-slot ring, the S waves run
-// tile s and the dP waves tile s - 1 (the slot loaded in step s + 1 is the
-// one tile s - 2 used), so there are n + 1 steps, each closed by the
-// workgroup barrier that publishes the next tile and the P just written.
+// faster over the whole backward. dS uses P rounded to bf16, as passed.)
+// The query tiles (and, with shared key/value heads, the tiles of every
+// head of the group in turn) form one stream; step s loads tile s + 1 into
+// a 3-slot ring, the S waves run tile s and the dP waves tile s - 1 (the
+// slot loaded in step s is the one tile s - 2 used), so there are n + 1
+// steps, each closed by the workgroup barrier that publishes the next tile
+// and the P just written.
 constexpr int kPairWaves = 8;
 constexpr int kPairSlots = 3;
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kPairWaves, 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ L2vec, const float* __restrict__ Dvec,
-                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                     int N, int n_kblocks, int n_kvheads, int group, float c2, float scale) {
+                const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                const float* __restrict__ L2vec, const float* __restrict__ Dvec,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                int N, int n_kblocks, int n_kvheads, int group, float c2, float scale) {
   using C = BwdCfg<D>;
   constexpr int NDMA = C::TILEB / 1024 / kPairWaves;  // wave-wide loads per wave and tensor
   static_assert(C::TILEB % (1024 * kPairWaves) == 0, "tile must split into whole wave-wide loads");
