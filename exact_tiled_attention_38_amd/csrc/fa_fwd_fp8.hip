@@ -123,9 +123,21 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
   const int G = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, jx = b >> 3, per = G >> 3, rem = G & 7;
   const int logical = xcd * per + min(xcd, rem) + jx;
-  const int bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
-  int t = logical - bh * n_qtiles;
-  if (CAUSAL) t = n_qtiles - 1 - t;
+  int bh, t;
+  // Causal, when each XCD's share is 4 or 8 whole heads: a group of 4 heads
+  // has its blocks go longest first across the 4, so the blocks that start
+  // last on an XCD are short ones. (With more heads per XCD the tail is a
+  // small part of the time and one head in flight per XCD keeps its L2 hits.)
+  if (CAUSAL && rem == 0 && per % (4 * n_qtiles) == 0 && per <= 8 * n_qtiles) {
+    const int gi = __builtin_amdgcn_readfirstlane(logical / (4 * n_qtiles));
+    const int r = logical - gi * 4 * n_qtiles;
+    bh = gi * 4 + (r & 3);
+    t = n_qtiles - 1 - (r >> 2);
+  } else {
+    bh = __builtin_amdgcn_readfirstlane(logical / n_qtiles);
+    t = logical - bh * n_qtiles;
+    if (CAUSAL) t = n_qtiles - 1 - t;
+  }
   const int q0 = __builtin_amdgcn_readfirstlane(t * C::BM);
   const int row0 = __builtin_amdgcn_readfirstlane(q0 + 32 * w);
   const int qrow = row0 + n;

@@ -57,6 +57,19 @@ def test_backward_small_shapes(N, d, causal):
     _check(q, k, v, do, dq, dk, dv, causal, scale, [(b, h) for b in range(B) for h in range(H)])
 
 
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 700, 128), (4, 16, 300, 64)])
+def test_backward_causal_heads_interleaved_on_each_xcd(B, H, N, d):
+    """32 or 64 heads of 256-row query blocks: each XCD's share of the dQ grid
+    is 4 or 8 whole heads, which the causal kernels issue longest block first
+    across groups of 4 heads. Every head's gradients are checked."""
+    _say("bwd interleaved heads", B, H, N, d)
+    cfg = dict(dtype="bf16", seed=900 + N + d)
+    q, k, v, do = W.make_inputs(cfg, DEV, with_do=True, shape=(B, H, N, d))
+    scale = 1 / math.sqrt(d)
+    _, _, dq, dk, dv = _run(q, k, v, do, True, scale)
+    _check(q, k, v, do, dq, dk, dv, True, scale, [(b, h) for b in range(B) for h in range(H)])
+
+
 def test_backward_nondefault_scale():
     _say("bwd scale 0.05")
     q, k, v, do = W.make_inputs(dict(dtype="bf16", seed=78), DEV, with_do=True, shape=(1, 2, 333, 128))

@@ -96,6 +96,24 @@ def test_fp8_small_shapes(N, H, Hkv, causal):
                         o[b, h].float().cpu().numpy(), lse[b, h].cpu().numpy(), scale, causal, what=f"head {(b, h)}")
 
 
+@pytest.mark.parametrize("B,H,Hkv,N", [(2, 16, 16, 700), (4, 16, 4, 300)])
+def test_fp8_causal_heads_interleaved_on_each_xcd(B, H, Hkv, N):
+    """32 or 64 query heads of 256-row blocks: each XCD's share of the grid is
+    4 or 8 whole heads, which the causal kernel issues longest block first
+    across groups of 4 heads. Every head is checked."""
+    _say("fp8 interleaved heads", B, H, Hkv, N)
+    d = 128
+    (q, k, v), (qd, kd, vd) = W.make_fp8_inputs(dict(seed=6100 + N + Hkv), DEV, shape=(B, H, N, d), kv_heads=Hkv)
+    scale = 1 / math.sqrt(d)
+    o, lse = forward_fp8(q, k, v, qd, kd, vd, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    g = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            _check_head(_codes(q[b, h]), _codes(k[b, h // g]), _codes(v[b, h // g]), qd, kd, vd,
+                        o[b, h].float().cpu().numpy(), lse[b, h].cpu().numpy(), scale, True, what=f"head {(b, h)}")
+
+
 def test_fp8_sharp_rows_and_large_values():
     """Q scaled so the rows are near one-hot; non-unit factors on every tensor."""
     _say("fp8 sharp")

@@ -272,3 +272,17 @@ def test_bf16_many_units_per_workgroup_deterministic(B, H, N, causal):
         torch.cuda.synchronize()
         assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
     _check_heads(q, k, v, first[0], first[1], scale, causal, [(B - 1, H - 1)])
+
+
+@pytest.mark.parametrize("B,H,N,d", [(2, 16, 700, 128), (4, 16, 300, 64), (2, 16, 513, 64)])
+def test_bf16_causal_heads_interleaved_on_each_xcd(B, H, N, d):
+    """32 or 64 heads of 256-row blocks: each XCD's share of the grid is 4 or
+    8 whole heads, which the causal forward issues longest block first across
+    groups of 4 heads. Every row of every head is checked."""
+    _say("interleaved heads", B, H, N, d)
+    cfg = dict(dtype="bf16", seed=77 + N + d, q_mult=4.0)
+    q, k, v = W.make_inputs(cfg, DEV, shape=(B, H, N, d))
+    scale = 1 / math.sqrt(d)
+    o, lse = forward(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _check_heads(q, k, v, o, lse, scale, True, [(b, h) for b in range(B) for h in range(H)])

@@ -60,6 +60,30 @@ def test_forward_small_shapes(N, H, Hkv, d, causal):
     assert torch.equal(o, o_rep) and torch.equal(lse, lse_rep)
 
 
+@pytest.mark.parametrize("B,H,Hkv,N", [(2, 16, 4, 700), (4, 16, 1, 300)])
+def test_causal_heads_interleaved_on_each_xcd(B, H, Hkv, N):
+    """32 or 64 query heads of 256-row blocks: each XCD's share of the grid
+    is 4 or 8 whole heads, which the causal forward and dQ kernels issue
+    longest block first across groups of 4 heads. Every head of the forward
+    and of the gradients is checked against the oracle."""
+    _say("gqa interleaved heads", B, H, Hkv, N)
+    d = 128
+    q, k, v, do = _inputs(B, H, Hkv, N, d, 2900 + N + Hkv, with_do=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = forward(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = backward(q, k, v, o, do, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, lse_ref = oracle.forward_heads(host(q[b]), host(k[b]), host(v[b]), scale, True)
+        assert_close(host(o[b]), o_ref, BF16_ATOL, BF16_RTOL, f"o batch {b}")
+        assert_close(host(lse[b]), lse_ref, LSE_ATOL, 0.0, f"lse batch {b}")
+        dq_ref, dk_ref, dv_ref = oracle.backward_heads(host(q[b]), host(k[b]), host(v[b]), host(do[b]),
+                                                       scale, True)[:3]
+        assert_close(host(dq[b]), dq_ref, GRAD_ATOL, GRAD_RTOL, f"dq batch {b}")
+        assert_close(host(dk[b]), dk_ref, GRAD_ATOL, GRAD_RTOL, f"dk batch {b}")
+        assert_close(host(dv[b]), dv_ref, GRAD_ATOL, GRAD_RTOL, f"dv batch {b}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (6, 3)])
