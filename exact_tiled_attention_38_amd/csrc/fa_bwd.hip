@@ -185,20 +185,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qd_off[i] = rr * C::ROWB + 16 * ((lane % C::CPR) ^ qswz<D>(rr));
   }
   // tile t of query head g of the group into ring slot `slot` (rows past N
-  // come from row N-1: finite, and masked)
+  // read as zeros through the buffer resources' range, and are masked)
   auto load_item = [&](int g, int t, int slot) {
     const int bh = kvbh * group + g;
     const int q0 = t * kBwdRows;
-    const char* qb = (const char*)(Q + ((size_t)bh * N + q0) * D);
-    const char* gb = (const char*)(dO + ((size_t)bh * N + q0) * D);
+    const uint32_t bytes = (uint32_t)min(N - q0, kBwdRows) * C::ROWB;
+    const i32x4_t qr = buffer_rsrc(Q + ((size_t)bh * N + q0) * D, bytes);
+    const i32x4_t gr = buffer_rsrc(dO + ((size_t)bh * N + q0) * D, bytes);
     FA_LDS char* dq_ = qdl + (2 * slot) * C::TILEB + w * NDMA * 1024;
     FA_LDS char* dg_ = qdl + (2 * slot + 1) * C::TILEB + w * NDMA * 1024;
     const int lim = N - 1 - q0;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
-      const uint32_t off = (uint32_t)min((int)(qd_off[i] / C::ROWB), lim) * C::ROWB + qd_off[i] % C::ROWB;
-      dma16(qb, off, dq_ + i * 1024);
-      dma16(gb, off, dg_ + i * 1024);
+      dma16_buf(qr, qd_off[i], dq_ + i * 1024);
+      dma16_buf(gr, qd_off[i], dg_ + i * 1024);
     }
     if (w < 2) {  // wave 0: the rows' lse * log2(e), wave 1: their D
       const char* src = (const char*)((w == 0 ? L2vec : Dvec) + (size_t)bh * N + q0);

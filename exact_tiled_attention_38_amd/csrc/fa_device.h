@@ -83,6 +83,25 @@ __device__ __forceinline__ void dma16_nt(const char* base, uint32_t voff, FA_LDS
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(voff), "s"(base), "s"(la) : "m0");
 }
+// The same through a buffer resource: lane i reads rsrc.base + voff, and a
+// lane whose 16 bytes lie past rsrc's size reads zeros instead of memory, so
+// a tile that runs past the end of a tensor needs no per-lane clamp. The
+// resource must be uniform (scalar registers).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4_t r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xffffu);  // stride 0: raw byte addressing
+  r[2] = (int32_t)bytes;                            // range checked against this
+  r[3] = 0x00020000;                                // 32-bit data format
+  return r;
+}
+__device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff, FA_LDS char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(la) : "m0");
+}
 __device__ __forceinline__ void dma4(const char* base, uint32_t voff, FA_LDS char* lds) {
   const uint32_t la = (uint32_t)(uintptr_t)lds;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"

@@ -60,8 +60,9 @@
 //     after a wave's rows is masked entirely (alpha = 1, P = 0, acc and l
 //     unchanged), which keeps the loop free of branches around the work.
 //   * Causal: the key range of a query block ends at its last row; only tiles
-//     touching the diagonal or the ragged tail (keys >= N) are masked. Tail
-//     rows are loaded from the clamped key N-1 (finite values) and masked.
+//     touching the diagonal or the ragged tail (keys >= N) are masked. The
+//     loads go through a buffer resource whose range ends at key N, so
+//     tail rows arrive as zeros (no per-lane clamp) and are masked.
 //   * Grid order: workgroups are dispatched round-robin over the 8 XCDs; the
 //     block index is remapped so each XCD works through whole heads (K/V of a
 //     head stay in that XCD's L2), longest causal query blocks first.
@@ -266,40 +267,31 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dk_off[i] = r * C::ROWB + 16 * (phys ^ kswz<D>(r));
     dv_off[i] = r * C::ROWB + 16 * (phys ^ vswz<D>(r));
   }
-  // rows past the last key (tail tile) are fetched from key N-1 instead:
-  // finite values that the mask then excludes
-  auto clamp_row = [&](uint32_t off, int lim) {
-    return (uint32_t)min((int)(off / C::ROWB), lim) * C::ROWB + (off % C::ROWB);
-  };
+  // rows past the last key (tail tile) read as zeros through the buffer
+  // resource's range; the mask excludes them
   // Tile t goes to ring slot t % S. Past the last tile the loads repeat the
   // last tile into the (unused) slot, so every step issues the same number
   // of loads and the wait count below is a constant.
   auto load_tile = [&](const uint16_t* src, int t, int slot0, const uint32_t (&off)[C::NDMA], int k0) __attribute__((always_inline)) {
     const int slot = slot0 + (t & (S - 1));
-    const char* base = (const char*)(src + (size_t)k0 * D);
+    const i32x4_t rsrc = buffer_rsrc(src + (size_t)k0 * D, (uint32_t)min(N - k0, BN) * C::ROWB);
     FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024;
-    if (k0 + BN <= N) {
 #pragma unroll
-      for (int i = 0; i < C::NDMA; ++i) dma16(base, off[i], dst + i * 1024);
-    } else {
-      const int lim = N - 1 - k0;
-#pragma unroll
-      for (int i = 0; i < C::NDMA; ++i) dma16(base, clamp_row(off[i], lim), dst + i * 1024);
-    }
+    for (int i = 0; i < C::NDMA; ++i) dma16_buf(rsrc, off[i], dst + i * 1024);
   };
   auto load_k = [&](int t, int k0) { load_tile(Kh, t, 0, dk_off, k0); };
   auto load_v = [&](int t, int k0) { load_tile(Vh, t, S, dv_off, k0); };
   // The same loads one wave-wide DMA at a time, so a step can spread them
   // over its matrix instructions: part j < NDMA is V tile vt's load j, the
-  // rest K tile kt's. Rows are always clamped (a no-op below the tail).
+  // rest K tile kt's.
   auto load_part = [&](int j, int vt, int vk0, int kt, int kk0) __attribute__((always_inline)) {
     const bool is_v = j < C::NDMA;
     const int i = is_v ? j : j - C::NDMA;
     const int k0 = is_v ? vk0 : kk0;
     const int slot = (is_v ? S : 0) + ((is_v ? vt : kt) & (S - 1));
-    const char* base = (const char*)((is_v ? Vh : Kh) + (size_t)k0 * D);
+    const i32x4_t rsrc = buffer_rsrc((is_v ? Vh : Kh) + (size_t)k0 * D, (uint32_t)min(N - k0, BN) * C::ROWB);
     FA_LDS char* dst = lds + slot * C::TILEB + w * C::NDMA * 1024 + i * 1024;
-    dma16(base, clamp_row(is_v ? dv_off[i] : dk_off[i], N - 1 - k0), dst);
+    dma16_buf(rsrc, is_v ? dv_off[i] : dk_off[i], dst);
   };
 
   // ---- Q^T operand: lane holds Q[qrow][16c + 8h .. +7]
