@@ -27,6 +27,7 @@ SHAPES = [
     (8, 32, 16384, 128, True),
     (1, 8, 100000, 128, True),
     (4, 16, 4096, 128, True),
+    (2, 16, 700, 128, True),  # 4 heads per XCD: blocks issued across groups of 4 heads
     (2, 2, 777, 64, True),
     (2, 2, 777, 64, False),
     (1, 3, 1, 128, True),
