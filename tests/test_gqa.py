@@ -192,3 +192,39 @@ def test_backward_deterministic():
         torch.cuda.synchronize()
         for a, b in zip(first, again):
             assert torch.equal(a, b)
+
+
+def _sweep_shapes(count, seed):
+    """Seeded random (B, H, Hkv, N, d, causal): head counts that put 1 to 8
+    whole heads (or fractions of heads) on each XCD, ragged and tiny N."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([1, 2, 3, 4]))
+        N = int(rng.choice([1, 33, 255, 256, 257, 511, 700, 1024, 1500, 2049]))
+        d = int(rng.choice([64, 128]))
+        out.append((B, H, Hkv, N, d, bool(rng.integers(2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", _sweep_shapes(48, 3838))
+def test_random_shapes_forward_and_backward(B, H, Hkv, N, d, causal):
+    """A seeded sweep over grid sizes, head sharing, ragged lengths and both
+    masks: every head's O, lse and gradients against the oracle."""
+    _say("sweep", B, H, Hkv, N, d, causal)
+    q, k, v, do = _inputs(B, H, Hkv, N, d, 4100 + N + 3 * H + Hkv + d + B, with_do=True)
+    scale = 1 / math.sqrt(d)
+    o, lse = forward(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = backward(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, lse_ref = oracle.forward_heads(host(q[b]), host(k[b]), host(v[b]), scale, causal)
+        assert_close(host(o[b]), o_ref, BF16_ATOL, BF16_RTOL, f"o batch {b}")
+        assert_close(host(lse[b]), lse_ref, LSE_ATOL, 0.0, f"lse batch {b}")
+        dq_ref, dk_ref, dv_ref = oracle.backward_heads(host(q[b]), host(k[b]), host(v[b]), host(do[b]),
+                                                       scale, causal)[:3]
+        assert_close(host(dq[b]), dq_ref, GRAD_ATOL, GRAD_RTOL, f"dq batch {b}")
+        assert_close(host(dk[b]), dk_ref, GRAD_ATOL, GRAD_RTOL, f"dk batch {b}")
+        assert_close(host(dv[b]), dv_ref, GRAD_ATOL, GRAD_RTOL, f"dv batch {b}")
