@@ -30,6 +30,9 @@ headline it carries, each timed in the same process:
                (TCC_EA0_RDREQ_DRAM_32B, TCC_EA0_WRREQ_WRITE_DRAM_32B, in
                32-byte units), scaled by their reading for a 1 GiB device copy
                and checked on the decode kernel, whose K/V bytes are known;
+  clocks       engine and memory clock (and board power where the driver
+               exposes it) sampled from the card's sysfs files while the
+               headline's timed launches run;
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload.
 """
 
@@ -409,12 +412,105 @@ def write_profile_records(outdir, paths, prof, launch_avg_ms):
 # ---------------------------------------------------------------- timing
 
 
-def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0):
+class ClockSampler:
+    """Engine and memory clock (and board power, where the driver exposes it)
+    read from the amdgpu sysfs files of this GPU's card every `period_s` on a
+    host thread while the timed launches run: pp_dpm_sclk / pp_dpm_mclk mark
+    the current level with '*'; hwmon power1_average / power1_input are in
+    microwatts. Plain file reads, no child process; silent if the files are
+    not there."""
+
+    def __init__(self, props, period_s=0.02):
+        import threading
+        self.period_s = period_s
+        self.card = self._card_dir(props)
+        self.samples = {"sclk_mhz": [], "mclk_mhz": [], "power_w": []}
+        self._stop = threading.Event()
+        self._thread = None
+
+    @staticmethod
+    def _card_dir(props):
+        want = (getattr(props, "pci_domain_id", None), getattr(props, "pci_bus_id", None),
+                getattr(props, "pci_device_id", None))
+        try:
+            names = sorted(n for n in os.listdir("/sys/class/drm") if n.startswith("card") and "-" not in n)
+        except OSError:
+            return None
+        for n in names:
+            dev = os.path.join("/sys/class/drm", n, "device")
+            try:
+                dom, bus, rest = os.path.basename(os.path.realpath(dev)).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    return dev
+            except (OSError, ValueError):
+                continue
+        return None
+
+    @staticmethod
+    def _current_level(path):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            pass
+        return None
+
+    def _power(self):
+        import glob
+        for name in ("power1_average", "power1_input"):
+            for f in glob.glob(os.path.join(self.card, "hwmon", "hwmon*", name)):
+                try:
+                    return int(open(f).read()) / 1e6
+                except (OSError, ValueError):
+                    pass
+        return None
+
+    def _read(self):
+        for key, f in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+            x = self._current_level(os.path.join(self.card, f))
+            if x is not None:
+                self.samples[key].append(x)
+        w = self._power()
+        if w is not None:
+            self.samples["power_w"].append(w)
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+        if self.card is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if self.card is None:
+            return {"error": "no amdgpu sysfs card matches this GPU's PCI address"}
+        out = {"source": f"amdgpu sysfs {os.path.basename(os.path.realpath(self.card))} (pp_dpm_sclk, "
+                         f"pp_dpm_mclk, hwmon power), sampled every {self.period_s * 1e3:.0f} ms on a host "
+                         f"thread during the timed launches"}
+        for key, xs in self.samples.items():
+            if xs:
+                s = sorted(xs)
+                out[key] = {"median": s[len(s) // 2], "min": s[0], "max": s[-1], "samples": len(s)}
+        return out
+
+
+def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0, sampler=None):
     """Run fn `warmup` times (and, with warm_ms, on until that much wall time
     has passed: a sub-millisecond kernel needs ~0.1 s of work before the
     clocks settle), then `steps` timed times, each bracketed by HIP events on
-    `stream`; `between` (untimed) runs before each timed launch. Returns (ms
-    of the whole timed region, per-launch ms list)."""
+    `stream`; `between` (untimed) runs before each timed launch; a
+    ClockSampler runs from the first timed launch to the end of the last.
+    Returns (ms of the whole timed region, per-launch ms list)."""
     import torch
 
     t0 = time.perf_counter()
@@ -431,6 +527,8 @@ def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if sampler is not None:
+        sampler.start()
     t_start.record(stream)
     for a, b in ev:
         if between is not None:
@@ -440,6 +538,8 @@ def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0):
         b.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
+    if sampler is not None:
+        sampler.stop()
     return t_start.elapsed_time(t_end), [a.elapsed_time(b) for a, b in ev]
 
 
@@ -977,13 +1077,14 @@ def main():
 
     log("timing the forward")
     fwd = lambda: fa.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
-    total_ms, per = time_launches(fwd, a.steps, a.warmup, stream)
+    props = torch.cuda.get_device_properties(dev)
+    sampler = ClockSampler(props)
+    total_ms, per = time_launches(fwd, a.steps, a.warmup, stream, sampler=sampler)
     ms = total_ms / a.steps
     flops = attention_flops(B, H, N, d, causal)
     tflops = flops / (ms * 1e-3) / 1e12
     per_sorted = sorted(per)
     launch_avg = sum(per) / len(per)
-    props = torch.cuda.get_device_properties(dev)
 
     result = {
         "metric": METRIC,
@@ -1025,6 +1126,7 @@ def main():
     }
     if Hkv != H:
         result["config"]["Hkv"] = Hkv
+    result["clocks"] = sampler.summary()
 
     if prof_dirs is not None:
         prof = headline_profile(prof_dirs["paths"], prof_dirs["errors"], launch_avg)

@@ -6,6 +6,8 @@ import csv
 import os
 import subprocess
 import sys
+import time
+import types
 
 import pytest
 
@@ -158,3 +160,25 @@ def test_ceiling_record_picks_the_gemm(tmp_path):
     assert float(rec["tflops"]) == pytest.approx(2 * 16384 ** 3 / 6e-3 / 1e12, rel=1e-3)
     assert float(rec["engine_clock_ghz"]) == pytest.approx(1.7, abs=1e-3)
     assert float(rec["mfma_busy_frac"]) == pytest.approx(0.7, abs=1e-4)
+
+
+def test_clock_sampler_reads_the_current_levels(tmp_path):
+    # the sysfs files' format: one "index: value unit" line per level, the
+    # current one marked with '*'; hwmon power in microwatts
+    card = tmp_path / "device"
+    (card / "hwmon" / "hwmon3").mkdir(parents=True)
+    (card / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1793Mhz *\n2: 2400Mhz\n")
+    (card / "pp_dpm_mclk").write_text("0: 900Mhz\n1: 2000Mhz *\n")
+    (card / "hwmon" / "hwmon3" / "power1_average").write_text("1360000000\n")
+    s = bench.ClockSampler(types.SimpleNamespace(pci_domain_id=-1, pci_bus_id=-1, pci_device_id=-1),
+                           period_s=0.001)
+    assert s.card is None
+    assert "error" in s.summary()
+    s.card = str(card)
+    s.start()
+    time.sleep(0.05)
+    s.stop()
+    out = s.summary()
+    assert out["sclk_mhz"]["median"] == 1793.0 and out["sclk_mhz"]["samples"] >= 1
+    assert out["mclk_mhz"]["max"] == 2000.0
+    assert out["power_w"]["min"] == 1360.0
