@@ -504,13 +504,17 @@ class ClockSampler:
         return out
 
 
-def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0, sampler=None):
+def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0, sampler=None, per_launch=True):
     """Run fn `warmup` times (and, with warm_ms, on until that much wall time
     has passed: a sub-millisecond kernel needs ~0.1 s of work before the
     clocks settle), then `steps` timed times, each bracketed by HIP events on
     `stream`; `between` (untimed) runs before each timed launch; a
     ClockSampler runs from the first timed launch to the end of the last.
-    Returns (ms of the whole timed region, per-launch ms list)."""
+    With per_launch=False only one event pair brackets the `steps`
+    back-to-back calls (each event record costs the stream ~5 us, which a
+    call of well under a millisecond would carry) and every entry of the
+    per-launch list is their mean. Returns (ms of the whole timed region,
+    per-launch ms list)."""
     import torch
 
     t0 = time.perf_counter()
@@ -529,6 +533,17 @@ def time_launches(fn, steps, warmup, stream, between=None, warm_ms=0.0, sampler=
     torch.cuda.synchronize()
     if sampler is not None:
         sampler.start()
+    if not per_launch:
+        assert between is None, "back-to-back timing has no untimed work between calls"
+        t_start.record(stream)
+        for _ in range(steps):
+            fn()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        if sampler is not None:
+            sampler.stop()
+        total = t_start.elapsed_time(t_end)
+        return total, [total / steps] * steps
     t_start.record(stream)
     for a, b in ev:
         if between is not None:
@@ -778,14 +793,15 @@ def bench_decode(a, cfg):
     ws = torch.empty(fa.decode_workspace_bytes(B, H, Hkv, Nq, Nk, d), dtype=torch.uint8, device=dev)
     scale = 1.0 / d ** 0.5
     step = lambda: fa.decode(q, k, v, causal=cfg["causal"], scale=scale, workspace=ws, out=o, lse=lse)
-    total_ms, per = time_launches(step, a.steps, a.warmup, stream, warm_ms=WARM_MS)
+    # eager calls back to back under one event pair: a call is 0.07-0.3 ms,
+    # and an event pair around each would add ~5 us of stream time to each
+    total_ms, per = time_launches(step, a.steps, a.warmup, stream, warm_ms=WARM_MS, per_launch=False)
     ms = total_ms / a.steps
     nbytes = decode_bytes(cfg)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    # A call is ~0.1 ms, about what the Python binding takes to issue it, so
-    # eager timing includes idle time between calls. Serving loops replay
-    # captured HIP graphs instead: time CALLS calls captured in one graph
-    # (the same kernels and arguments), which measures the kernels' own time.
+    # Serving loops replay captured HIP graphs: time CALLS calls captured in
+    # one graph (the same kernels and arguments), which leaves out the gaps
+    # between eagerly issued kernels.
     calls = 10
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
