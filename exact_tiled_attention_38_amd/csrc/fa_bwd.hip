@@ -44,6 +44,7 @@ constexpr int kBwdRows = 64;              // query rows per tile
 
 // The dK/dV grid walks key/value heads in chunks of this many (one per XCD).
 constexpr int kBwdHeadChunk = 8;
+static_assert(kBwdHeadChunk == 8, "the grid order maps head chunks onto the 8 XCDs");
 
 // Q and dO tiles (kBwdRows rows) arrive by direct-to-LDS loads into a
 // ring, unpadded, with the 16-byte chunks of each row XOR-swizzled
@@ -145,11 +146,26 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // workgroup b runs on XCD b % 8, so each XCD keeps to one head of the chunk
   // and its concurrent key blocks share that head's query tiles in L2, and
   // under a causal mask the longest key blocks (the first ones) start first.
-  const int chunk = blockIdx.x / (kBwdHeadChunk * n_kblocks);
-  const int r = blockIdx.x - chunk * (kBwdHeadChunk * n_kblocks);
-  const int cc = min(kBwdHeadChunk, n_kvheads - kBwdHeadChunk * chunk);
-  const int kbi = r / cc;
-  const int kvbh = __builtin_amdgcn_readfirstlane(kBwdHeadChunk * chunk + r - kbi * cc);
+  // Small causal launches (each XCD holding 4 or 8 heads and at most 256
+  // workgroups, 8 per compute unit) take each XCD's heads 4 at a time with
+  // their key blocks longest first across the 4, so the blocks that start
+  // last are short ones (the causal B4 H16 N4096 backward: 2.4 % faster,
+  // bitwise the same); with more work per unit the tail weighs little and
+  // one head per XCD keeps its query tiles in L2.
+  int kbi, kvbh;
+  if (CAUSAL && n_kvheads % (4 * kBwdHeadChunk) == 0 && n_kvheads <= 8 * kBwdHeadChunk &&
+      n_kvheads / kBwdHeadChunk * n_kblocks <= 256) {
+    const int x = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    const int g = jx / (4 * n_kblocks), rr = jx - g * 4 * n_kblocks;
+    kbi = __builtin_amdgcn_readfirstlane(rr >> 2);
+    kvbh = __builtin_amdgcn_readfirstlane((4 * g + (rr & 3)) * kBwdHeadChunk + x);
+  } else {
+    const int chunk = blockIdx.x / (kBwdHeadChunk * n_kblocks);
+    const int r = blockIdx.x - chunk * (kBwdHeadChunk * n_kblocks);
+    const int cc = min(kBwdHeadChunk, n_kvheads - kBwdHeadChunk * chunk);
+    kbi = __builtin_amdgcn_readfirstlane(r / cc);
+    kvbh = __builtin_amdgcn_readfirstlane(kBwdHeadChunk * chunk + r - kbi * cc);
+  }
   const int kb0 = __builtin_amdgcn_readfirstlane(kbi * kBwdKeys);
   const int key = kb0 + 32 * kg + n;
   const size_t head = (size_t)kvbh * N * D;

@@ -61,7 +61,8 @@ def test_backward_small_shapes(N, d, causal):
 def test_backward_causal_heads_interleaved_on_each_xcd(B, H, N, d):
     """32 or 64 heads of 256-row query blocks: each XCD's share of the dQ grid
     is 4 or 8 whole heads, which the causal kernels issue longest block first
-    across groups of 4 heads. Every head's gradients are checked."""
+    across groups of 4 heads (the dK/dV kernel its 128-key blocks likewise).
+    Every head's gradients are checked."""
     _say("bwd interleaved heads", B, H, N, d)
     cfg = dict(dtype="bf16", seed=900 + N + d)
     q, k, v, do = W.make_inputs(cfg, DEV, with_do=True, shape=(B, H, N, d))

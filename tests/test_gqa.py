@@ -60,12 +60,14 @@ def test_forward_small_shapes(N, H, Hkv, d, causal):
     assert torch.equal(o, o_rep) and torch.equal(lse, lse_rep)
 
 
-@pytest.mark.parametrize("B,H,Hkv,N", [(2, 16, 4, 700), (4, 16, 1, 300)])
+@pytest.mark.parametrize("B,H,Hkv,N", [(2, 16, 4, 700), (4, 16, 1, 300), (4, 16, 8, 700)])
 def test_causal_heads_interleaved_on_each_xcd(B, H, Hkv, N):
     """32 or 64 query heads of 256-row blocks: each XCD's share of the grid
     is 4 or 8 whole heads, which the causal forward and dQ kernels issue
-    longest block first across groups of 4 heads. Every head of the forward
-    and of the gradients is checked against the oracle."""
+    longest block first across groups of 4 heads; with 32 key/value heads
+    (4, 16, 8, 700) the dK/dV kernel does the same with its key blocks.
+    Every head of the forward and of the gradients is checked against the
+    oracle."""
     _say("gqa interleaved heads", B, H, Hkv, N)
     d = 128
     q, k, v, do = _inputs(B, H, Hkv, N, d, 2900 + N + Hkv, with_do=True)
