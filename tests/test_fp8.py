@@ -219,3 +219,38 @@ def test_fp8_score_error_margin():
     margin = max(ratios)
     print(f"[fp8 margin] largest score error on near one-hot rows / delta = {margin:.3f}", flush=True)
     assert margin < 1.0
+
+
+def _fp8_sweep(count, seed):
+    """Seeded random (B, H, Hkv, N, causal, scale, factor multipliers): head
+    counts that put fractions of a head up to 8 whole heads on each XCD,
+    ragged and tiny N, non-default scales and dequantisation factors."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([1, 2, 3, 4]))
+        N = int(rng.choice([1, 33, 64, 65, 255, 256, 257, 511, 700, 1025, 1500]))
+        scale = float(rng.choice([0.05, 1 / math.sqrt(128), 0.15]))
+        mult = tuple(float(x) for x in 2.0 ** rng.uniform(-2, 2, size=3))
+        out.append((B, H, Hkv, N, bool(rng.integers(2)), scale, mult))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,causal,scale,mult", _fp8_sweep(24, 3939))
+def test_fp8_random_shapes(B, H, Hkv, N, causal, scale, mult):
+    """A seeded sweep over grid sizes, head sharing, ragged lengths, both
+    masks, scales and dequantisation factors: every head against the oracle
+    within the bound derived above."""
+    _say("fp8 sweep", B, H, Hkv, N, causal, scale, mult)
+    d = 128
+    (q, k, v), f = W.make_fp8_inputs(dict(seed=6400 + N + 3 * H + Hkv + B), DEV, shape=(B, H, N, d), kv_heads=Hkv)
+    qd, kd, vd = (x * m for x, m in zip(f, mult))
+    o, lse = forward_fp8(q, k, v, qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    g = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            _check_head(_codes(q[b, h]), _codes(k[b, h // g]), _codes(v[b, h // g]), qd, kd, vd,
+                        o[b, h].float().cpu().numpy(), lse[b, h].cpu().numpy(), scale, causal, what=f"head {(b, h)}")

@@ -159,3 +159,34 @@ def test_bench_workload_sampled_rows():
                                                      rp, cc, BM, BN, rows=rows)
         assert_close(host(o[b, h])[rows], o_ref, BF16_ATOL, BF16_RTOL, f"o head {(b, h)}")
         assert_close(host(lse[b, h])[rows], lse_ref, LSE_ATOL, 0.0, f"lse head {(b, h)}")
+
+
+def _sparse_sweep(count, seed):
+    """Seeded random (B, H, Hkv, N, d, causal, density, shuffle, empty_every)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([1, 2, 3]))
+        N = int(rng.choice([1, 63, 64, 65, 255, 256, 257, 700, 1025, 1500]))
+        d = int(rng.choice([64, 128]))
+        out.append((B, H, Hkv, N, d, bool(rng.integers(2)), float(rng.choice([0.1, 0.3, 0.6, 1.0])),
+                    bool(rng.integers(2)), int(rng.choice([0, 3, 7]))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal,density,shuffle,empty_every", _sparse_sweep(24, 4040))
+def test_block_sparse_random_shapes(B, H, Hkv, N, d, causal, density, shuffle, empty_every):
+    """A seeded sweep over grid sizes, head sharing, ragged lengths, both
+    masks, list densities and orders, and empty lists: every head against the
+    oracle."""
+    _say("sparse sweep", B, H, Hkv, N, d, causal, density, shuffle, empty_every)
+    rng = np.random.default_rng(5300 + N + 3 * H + Hkv + d + B)
+    q, k, v = W.make_inputs(dict(dtype="bf16", seed=5400 + N + H + d), DEV, shape=(B, H, N, d), kv_heads=Hkv)
+    n_qb, n_kb = -(-N // BM), -(-N // BN)
+    row_ptr, cols = _selection(rng, B * H * n_qb, n_kb, density, shuffle, empty_every=empty_every)
+    scale = 1 / math.sqrt(d)
+    o, lse = forward_block_sparse(q, k, v, _dev(row_ptr), _dev(cols), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    _check(q, k, v, o, lse, causal, scale, row_ptr, cols)
