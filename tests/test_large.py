@@ -40,6 +40,8 @@ def test_heads_past_4_gib_match_single_head_calls():
                                  ("dv", dv, dv1)):
             part = big[b:b + 1, h:h + 1]
             assert torch.equal(part, small), f"{name} of head {(b, h)} differs from the single-head call"
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
 
 
 def test_fp8_heads_past_4_gib_match_single_head_calls():
@@ -56,6 +58,8 @@ def test_fp8_heads_past_4_gib_match_single_head_calls():
         torch.cuda.synchronize()
         assert torch.equal(o[b:b + 1, h:h + 1], o1), f"o of head {(b, h)} differs from the single-head call"
         assert torch.equal(lse[b:b + 1, h:h + 1], lse1), f"lse of head {(b, h)} differs from the single-head call"
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
 
 
 def test_decode_cache_past_4_gib():
@@ -71,3 +75,5 @@ def test_decode_cache_past_4_gib():
         o_ref, lse_ref = oracle.forward_decode(host(q[b, h]), host(k[b, h]), host(v[b, h]), scale, True)
         assert_close(host(o[b, h]), o_ref, BF16_ATOL, BF16_RTOL, f"o head {(b, h)}")
         assert_close(host(lse[b, h]), lse_ref, LSE_ATOL, 0.0, f"lse head {(b, h)}")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
