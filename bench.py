@@ -17,6 +17,9 @@ headline it carries, each timed in the same process:
                causal B4 H16 N4096;
   worst_case   the forward on rising-score inputs, where the fast pass's
                row-sum bound fails in every query block;
+  widened      decode (100K- and 16K-token caches), the fp8 forward, the
+               block-sparse forward and 8 shared key/value heads, each timed
+               as its own --workload line would, with fewer steps;
   ceiling      the vendor bf16 GEMM at 16384^3 (what a plain matrix product
                reaches on this part);
   roofline     the forward against the dense-bf16 matrix peak (2516.6 TFLOP/s
@@ -1019,6 +1022,55 @@ def bench_other_configs(a, dev, stream, headline_launch_avg_ms):
     return out
 
 
+def bench_widened(a):
+    """The widened rows in the same invocation, briefly: decode at the 100K-token
+    and 16K caches, the fp8 forward, the block-sparse forward and the forward
+    with 8 shared key/value heads, each as its own `--workload` line would
+    time it (fewer steps), reduced to its figures and roofline fraction."""
+    import torch
+
+    import exact_tiled_attention_38_amd as fa
+    from exact_tiled_attention_38_amd import workloads as W
+
+    sub = argparse.Namespace(**vars(a))
+    sub.steps, sub.warmup = max(5, min(a.steps, 10)), 2
+    out = {}
+
+    def keep(name, r):
+        out[name] = {"workload": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
+                     "ms_per_step": r["ms_per_step"], "roofline_frac": r["roofline"]["frac"],
+                     "roofline_peak": r["roofline"]["peak"], "launch_avg_ms": r["roofline"]["launch_avg_ms"]}
+
+    for name, fn in (("decode_long", lambda: bench_decode(sub, W.DECODE_WORKLOADS["decode_long"])),
+                     ("decode", lambda: bench_decode(sub, W.DECODE_WORKLOADS["decode"])),
+                     ("fp8", lambda: bench_fp8(sub, W.FP8_WORKLOADS["fp8"])),
+                     ("sparse", lambda: bench_sparse(sub, W.SPARSE_WORKLOADS["sparse"]))):
+        try:
+            keep(name, fn())
+        except RuntimeError as e:
+            out[name] = {"error": str(e)}
+        torch.cuda.empty_cache()
+    try:
+        cfg = W.gqa_config("gqa")
+        dev = torch.device("cuda:0")
+        q, k, v = W.make_inputs(cfg, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fl = attention_flops(cfg["B"], cfg["H"], cfg["N"], cfg["d"], cfg["causal"])
+        _, per = time_launches(lambda: fa.forward(q, k, v, causal=cfg["causal"], scale=cfg["scale"], out=o, lse=lse),
+                               sub.steps, sub.warmup, torch.cuda.current_stream(dev), warm_ms=WARM_MS)
+        e = _fwd_entry(per, fl)
+        out["gqa"] = {"workload": f"causal bf16 forward, B={cfg['B']} H={cfg['H']} Hkv={cfg['Hkv']} "
+                                  f"N={cfg['N']} d={cfg['d']}", "value": e["tflops"], "unit": "TFLOP/s",
+                      "ms_per_step": e["launch_avg_ms"], "roofline_frac": e["frac_of_peak"],
+                      "roofline_peak": PEAK_BF16_TFLOPS, "launch_avg_ms": e["launch_avg_ms"]}
+        del q, k, v, o, lse
+    except RuntimeError as e:
+        out["gqa"] = {"error": str(e)}
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---------------------------------------------------------------- main
 
 
@@ -1195,6 +1247,8 @@ def main():
         log("timing the other configurations and the worst case")
         result["configs"] = bench_other_configs(a, dev, stream, launch_avg)
         result["worst_case"] = result["configs"].pop("worst_case")
+        log("timing the widened rows (decode, fp8, block-sparse, shared heads)")
+        result["widened"] = bench_widened(a)
 
     if not a.no_cpu_baseline and a.workload != "rising":
         log("timing the CPU oracle")
